@@ -1,0 +1,196 @@
+/*
+ * nsg.h — batched Newton–Schulz / Gram Newton–Schulz orthogonalization on
+ * AMD Instinct MI355X (gfx950).  C ABI of libnsg.so.
+ *
+ * What is computed (the pages' notation: n <= m, alpha = m / n):
+ *   For every matrix G_g of a bucket [G, R, C]:
+ *     X  = G_g       if R <= C,   X = G_g^T  otherwise (short side leads;
+ *          "muon" kernel card, "How it works")
+ *     X0 = X / (s (||X||_F + eps))            (Dion3 paper, Alg. 1 / Alg. 3 step 2;
+ *                                              safety factor s, App. B.2.2)
+ *     NSG_STANDARD: T steps of  A = X X^T,  B = b_t A + c_t A^2,  X = a_t X + B X
+ *                   (Dion3 paper, Section 2.2, Algorithm 1)
+ *     NSG_GRAM:     R = X0 X0^T, Q = I, T steps of
+ *                     Z = b_t R + c_t R^2,  Q = Q Z + a_t Q,
+ *                     RZ = R Z + a_t R,     R = Z RZ + a_t RZ
+ *                   with one restart (X = Q X, R = X X^T, Q = I) at the top of
+ *                   step restart_after + 1, output Q X
+ *                   (Dion3 paper, Section 4.2, Algorithm 3; the a*I terms are
+ *                   applied in fp32 epilogues, never stored: Appendix B.2.3).
+ *                   A square matrix (m == n) runs NSG_STANDARD instead
+ *                   (Dion3 paper, Section 4.1, last paragraph).
+ *     out_g = result (transposed back when R > C).
+ *
+ * Arithmetic: GEMM operands and every intermediate matrix are stored in the
+ * compute dtype (fp16 by default, Alg. 3 step 3; bf16; or fp32 for the debug
+ * path); products accumulate in fp32 and every epilogue (scales, a*X, a*Q,
+ * a*R, a*RZ, the +a*I of a fresh Q) runs in fp32, rounding once to the
+ * storage dtype (round to nearest even).  The Frobenius norm is a fixed-order
+ * fp32 sum of squares.  Results depend only on (matrix, shape, parameters),
+ * never on G or on the other matrices of the bucket.
+ *
+ * Conventions for every call below:
+ *   - Memory: every pointer marked "device" is device memory owned by the
+ *     caller; the library allocates nothing, frees nothing and never blocks
+ *     the host.  ns_orthogonalize only enqueues work on `stream`.
+ *   - Errors: argument problems are reported before anything is enqueued and
+ *     leave `out` untouched.  A failed kernel launch returns NSG_ERR_HIP.
+ *     Numerical blow-up is not an error: it is reported per matrix in
+ *     `status` (when given).
+ *   - Thread safety: calls are reentrant; concurrent calls need distinct
+ *     workspaces.  The optional launch timing (ns_timing_*) is process-global.
+ */
+#ifndef NSG_H_
+#define NSG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NSG_OK = 0,
+  NSG_ERR_INVALID_ARG = 1,         /* null pointer, bad enum, bad steps/coeffs/safety */
+  NSG_ERR_UNSUPPORTED_DTYPE = 2,   /* dtype code outside nsg_dtype_t */
+  NSG_ERR_SHAPE = 3,               /* negative size, or a side above NSG_MAX_SIDE */
+  NSG_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace null, misaligned or too small */
+  NSG_ERR_HIP = 5                  /* a HIP runtime call or kernel launch failed */
+} nsg_status_t;
+
+typedef enum { NSG_F16 = 0, NSG_BF16 = 1, NSG_F32 = 2 } nsg_dtype_t;
+
+typedef enum {
+  NSG_STANDARD = 0, /* Algorithm 1 */
+  NSG_GRAM = 1      /* Algorithm 3; square matrices fall back to Algorithm 1 */
+} nsg_mode_t;
+
+#define NSG_MAX_SIDE 65536 /* largest R or C accepted */
+#define NSG_MAX_STEPS 64
+#define NSG_WORKSPACE_ALIGN 256
+
+typedef struct {
+  int32_t steps;          /* T >= 1 (Muon: 5) */
+  const double *coeffs;   /* host: 3 values (a, b, c) used at every step, or
+                             3*steps values a_1,b_1,c_1,...; read during the
+                             call only.  "muon" kernel card: (3.4445, -4.7750,
+                             2.0315) */
+  int32_t n_coeffs;       /* 3 or 3*steps */
+  int32_t mode;           /* nsg_mode_t */
+  int32_t restart_after;  /* NSG_GRAM: restart at the top of step
+                             restart_after + 1 (Alg. 3: 2); 0, or >= steps,
+                             means no restart (Alg. 2) */
+  float safety;           /* s > 0 in X / (s (||X||_F + eps)); App. B.2.2
+                             recommends 1.05 for Gram NS */
+  float eps;              /* >= 0; Alg. 1: 1e-7 */
+  int32_t compute_dtype;  /* nsg_dtype_t: F16 (Alg. 3), BF16 (Alg. 1), or F32
+                             (debug path) */
+} nsg_params_t;
+
+/* Fills *p with the defaults: steps 5, the Muon triple, NSG_GRAM,
+ * restart_after 2, safety 1.05, eps 1e-7, fp16 compute.  The coefficient
+ * pointer refers to static storage inside the library. */
+void ns_default_params(nsg_params_t *p);
+
+/* Bytes of device workspace ns_orthogonalize needs for a bucket of G
+ * matrices of R x C with parameters *p.  Host only; no GPU needed.
+ * Returns NSG_OK and writes *bytes (0 for an empty bucket), or an argument
+ * error as ns_orthogonalize would. */
+nsg_status_t ns_workspace_size(int64_t G, int64_t R, int64_t C,
+                               const nsg_params_t *p, size_t *bytes);
+
+/* Orthogonalize a bucket.
+ *   in      device, [G, R, C] row-major contiguous, dtype in_dtype; read only.
+ *   out     device, [G, R, C] row-major contiguous, dtype out_dtype; may be
+ *           the same memory as `in` (the input is fully consumed into the
+ *           workspace before the first output write).
+ *   workspace  device, at least ns_workspace_size bytes, aligned to
+ *           NSG_WORKSPACE_ALIGN; contents on entry are ignored and on exit
+ *           undefined.
+ *   status  device, G int32 values, or NULL.  Set to 0 for a matrix whose
+ *           output is all finite, 1 otherwise.
+ *   stream  hipStream_t to enqueue on (NULL = the default stream).
+ * G == 0, R == 0 or C == 0 returns NSG_OK and enqueues nothing. */
+nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype,
+                              void *out, int32_t out_dtype,
+                              int64_t G, int64_t R, int64_t C,
+                              const nsg_params_t *p,
+                              void *workspace, size_t workspace_bytes,
+                              int32_t *status, void *stream);
+
+/* Static text for a status code. */
+const char *ns_status_string(nsg_status_t s);
+
+/* FLOPs per matrix of an R x C bucket, host only.
+ *   credited: the pages' formula for the algorithm that runs —
+ *             2T(2 alpha + 1) n^3 for standard NS (Dion3 paper, Section 2.2),
+ *             (4T + 6 alpha - 6) n^3 for Gram NS with one restart
+ *             (Section 4.1 plus 3(alpha - 1) n^3, Section 4.2), and
+ *             (4T + 3 alpha - 3) n^3 without a restart (Section 4.1);
+ *   executed: 2 M N K summed over the tiles the launch plan actually runs
+ *             (symmetric products count only their lower-triangle tiles;
+ *             padding to whole tiles included). */
+nsg_status_t ns_flops(int64_t R, int64_t C, const nsg_params_t *p,
+                      double *credited, double *executed);
+
+/* One entry of the launch plan (host only): what each kernel launch of a
+ * call does, per matrix. */
+typedef struct {
+  int32_t kind;     /* 0 norm reduce, 1 scale/cast/transpose, 2 general GEMM,
+                       3 symmetric GEMM */
+  int32_t step;     /* NS step t (1..T); 0 before the loop, T+1 for the output */
+  int64_t M, N, K;  /* GEMM logical sizes (0 for the normalize kernels) */
+  double flops;     /* executed FLOPs per matrix (tiles run, 2MNK per tile) */
+  double bytes;     /* algorithmic HBM bytes per matrix: operands read once,
+                       outputs written once */
+  char label[24];   /* e.g. "R0=XXt", "Z", "Q=QZ+aQ", "RZ", "R=Z.RZ", "Y=QX" */
+} nsg_launch_info_t;
+
+/* Writes up to max_entries launch descriptions for one call on an R x C
+ * bucket and the total count to *count (host only). */
+nsg_status_t ns_plan(int64_t R, int64_t C, const nsg_params_t *p,
+                     nsg_launch_info_t *entries, int32_t max_entries,
+                     int32_t *count);
+
+/* Optional per-launch timing with HIP events, for the benchmark's roofline.
+ * ns_timing_enable(1) makes every later ns_orthogonalize call record a
+ * hipEvent before and after each of its kernel launches, on the stream the
+ * kernels run on.  ns_timing_collect waits for the recorded events, writes up
+ * to max_entries (kind, milliseconds) pairs in launch order, sets *count to
+ * the number recorded since the last collect or enable, and clears them.
+ * Timing is process-global and meant for single-threaded benchmarking. */
+nsg_status_t ns_timing_enable(int32_t on);
+nsg_status_t ns_timing_collect(int32_t *kinds, float *ms, int32_t max_entries,
+                               int32_t *count);
+
+/* Plain device-to-device copy kernel (16-byte vector loads/stores), used to
+ * calibrate hardware byte counters against a known traffic.  src and dst are
+ * device pointers of `bytes` bytes each, 16-byte aligned, not overlapping. */
+nsg_status_t nsg_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+
+/* Building block, exposed for testing the GEMM kernels on their own.
+ * For b in [0, batch):  V = alpha * A_b B_b^T + beta * Cin_b   (fp32), then
+ *   out_b   = V           (row-major M x N, ld ldo)       if out   != NULL
+ *   out_t_b = V^T         (row-major N x M, ld ldt)       if out_t != NULL
+ *   out_d_b = V + diag*I  (row-major M x N, ld ldo)       if out_d != NULL
+ * A_b is M x K (ld lda), B_b is N x K (ld ldb), Cin_b is M x N (ld ldc);
+ * operands, Cin and outputs are in `dtype`; batches are contiguous
+ * ([batch][rows][ld]).  symmetric != 0 computes only the tiles on or below
+ * the diagonal and mirrors them (requires M == N and out_t == NULL); the
+ * result is then exactly symmetric (the symmetric GEMM of the Dion3 paper,
+ * Section 5 and Appendix C.1).  M, N and K must be multiples of 256.
+ * All pointers are device memory; 16-byte aligned. */
+nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch,
+                         int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda, const void *B, int64_t ldb,
+                         float alpha, float beta, const void *Cin, int64_t ldc,
+                         void *out, int64_t ldo, void *out_t, int64_t ldt,
+                         void *out_d, float diag, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSG_H_ */

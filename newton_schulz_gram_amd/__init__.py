@@ -1,0 +1,264 @@
+"""newton_schulz_gram_amd — batched Newton–Schulz / Gram Newton–Schulz on MI355X.
+
+A thin ctypes binding over libnsg.so (include/nsg.h).  Every step of the
+orthogonalization runs in the library's gfx950 HIP kernels; this module only
+checks and marshals arguments, takes device memory and the current stream from
+PyTorch, and raises if the library is missing or a call fails.  There is no
+CPU fallback.
+
+    import torch, newton_schulz_gram_amd as nsg
+    O = nsg.orthogonalize(G)            # G: [R, C] or [G, R, C] on the GPU
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnsg.so")
+
+NSG_F16, NSG_BF16, NSG_F32 = 0, 1, 2
+NSG_STANDARD, NSG_GRAM = 0, 1
+MUON_COEFFS = (3.4445, -4.7750, 2.0315)  # "muon" kernel card, "How it works"
+
+_DT = {torch.float16: NSG_F16, torch.bfloat16: NSG_BF16, torch.float32: NSG_F32}
+_DT_NAMES = {"f16": NSG_F16, "fp16": NSG_F16, "float16": NSG_F16,
+             "bf16": NSG_BF16, "bfloat16": NSG_BF16,
+             "f32": NSG_F32, "fp32": NSG_F32, "float32": NSG_F32}
+_MODES = {"standard": NSG_STANDARD, "gram": NSG_GRAM}
+KIND_NAMES = {0: "norm_reduce", 1: "scale_cast_transpose", 2: "gemm_nt", 3: "gemm_nt_sym"}
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype", 3: "unsupported shape",
+          4: "workspace missing, misaligned or too small", 5: "HIP runtime error"}
+
+
+class NSGError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, 'status %d' % code)} (nsg status {code})")
+        self.code = code
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("steps", ctypes.c_int32),
+        ("coeffs", ctypes.POINTER(ctypes.c_double)),
+        ("n_coeffs", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("restart_after", ctypes.c_int32),
+        ("safety", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("compute_dtype", ctypes.c_int32),
+    ]
+
+
+class LaunchInfo(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("step", ctypes.c_int32),
+        ("M", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("flops", ctypes.c_double),
+        ("bytes", ctypes.c_double),
+        ("label", ctypes.c_char * 24),
+    ]
+
+
+EXPORTS = ("ns_default_params", "ns_workspace_size", "ns_orthogonalize", "ns_status_string",
+           "ns_flops", "ns_plan", "ns_timing_enable", "ns_timing_collect", "nsg_copy",
+           "nsg_gemm_nt")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnsg.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libnsg.so is not built ({LIB_PATH}); run "
+                           "`python -m newton_schulz_gram_amd.build` or __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER(Params)
+    L.ns_default_params.argtypes = [P]
+    L.ns_default_params.restype = None
+    L.ns_workspace_size.argtypes = [i64, i64, i64, P, ctypes.POINTER(sz)]
+    L.ns_workspace_size.restype = i32
+    L.ns_orthogonalize.argtypes = [vp, i32, vp, i32, i64, i64, i64, P, vp, sz, vp, vp]
+    L.ns_orthogonalize.restype = i32
+    L.ns_status_string.argtypes = [i32]
+    L.ns_status_string.restype = ctypes.c_char_p
+    L.ns_flops.argtypes = [i64, i64, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    L.ns_flops.restype = i32
+    L.ns_plan.argtypes = [i64, i64, P, ctypes.POINTER(LaunchInfo), i32, ctypes.POINTER(i32)]
+    L.ns_plan.restype = i32
+    L.ns_timing_enable.argtypes = [i32]
+    L.ns_timing_enable.restype = i32
+    L.ns_timing_collect.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]
+    L.ns_timing_collect.restype = i32
+    L.nsg_copy.argtypes = [vp, vp, sz, vp]
+    L.nsg_copy.restype = i32
+    L.nsg_gemm_nt.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp, i64, f32, f32, vp, i64,
+                              vp, i64, vp, i64, vp, f32, vp]
+    L.nsg_gemm_nt.restype = i32
+    _lib = L
+    return L
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise NSGError(code, what)
+
+
+def _dtype_code(dt) -> int:
+    if isinstance(dt, str):
+        return _DT_NAMES[dt]
+    if isinstance(dt, torch.dtype):
+        if dt not in _DT:
+            raise TypeError(f"unsupported dtype {dt}")
+        return _DT[dt]
+    return int(dt)
+
+
+def make_params(steps: int = 5, coeffs: Optional[Sequence[float]] = None, mode: str = "gram",
+                restart_after: int = 2, safety: float = 1.05, eps: float = 1e-7,
+                compute_dtype="f16"):
+    """Build an nsg_params_t.  Returns (params, keepalive) — keep both alive."""
+    c = list(MUON_COEFFS if coeffs is None else coeffs)
+    arr = (ctypes.c_double * len(c))(*[float(x) for x in c])
+    p = Params()
+    p.steps = int(steps)
+    p.coeffs = ctypes.cast(arr, ctypes.POINTER(ctypes.c_double))
+    p.n_coeffs = len(c)
+    p.mode = _MODES[mode] if isinstance(mode, str) else int(mode)
+    p.restart_after = int(restart_after)
+    p.safety = float(safety)
+    p.eps = float(eps)
+    p.compute_dtype = _dtype_code(compute_dtype)
+    return p, arr
+
+
+def workspace_size(G: int, R: int, C: int, **kw) -> int:
+    p, _keep = make_params(**kw)
+    out = ctypes.c_size_t(0)
+    _check(lib().ns_workspace_size(G, R, C, ctypes.byref(p), ctypes.byref(out)), "ns_workspace_size")
+    return int(out.value)
+
+
+def flops(R: int, C: int, **kw):
+    """(credited, executed) FLOPs per matrix (the pages' formula; the plan's tiles)."""
+    p, _keep = make_params(**kw)
+    cr, ex = ctypes.c_double(0), ctypes.c_double(0)
+    _check(lib().ns_flops(R, C, ctypes.byref(p), ctypes.byref(cr), ctypes.byref(ex)), "ns_flops")
+    return cr.value, ex.value
+
+
+def plan(R: int, C: int, **kw):
+    """The launch list of one call, as a list of dicts (host only)."""
+    p, _keep = make_params(**kw)
+    n = ctypes.c_int32(0)
+    _check(lib().ns_plan(R, C, ctypes.byref(p), None, 0, ctypes.byref(n)), "ns_plan")
+    arr = (LaunchInfo * max(1, n.value))()
+    _check(lib().ns_plan(R, C, ctypes.byref(p), arr, n.value, ctypes.byref(n)), "ns_plan")
+    return [dict(kind=e.kind, kernel=KIND_NAMES[e.kind], step=e.step, M=e.M, N=e.N, K=e.K,
+                 flops=e.flops, bytes=e.bytes, label=e.label.decode()) for e in arr[:n.value]]
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def orthogonalize(G: torch.Tensor, steps: int = 5, coeffs: Optional[Sequence[float]] = None,
+                  mode: str = "gram", restart_after: int = 2, safety: float = 1.05,
+                  eps: float = 1e-7, compute_dtype="f16", out_dtype=None,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Orthogonalize one matrix [R, C] or a bucket [G, R, C] on its GPU.
+
+    Returns `out` (allocated if not given) with dtype out_dtype (default: the
+    input's).  `status`, if given, is an int32 CUDA tensor of G entries set to
+    1 for matrices whose output has a non-finite value.
+    """
+    if not G.is_cuda:
+        raise ValueError("orthogonalize needs a GPU tensor (no CPU path)")
+    squeeze = G.dim() == 2
+    Gs = G.unsqueeze(0) if squeeze else G
+    if Gs.dim() != 3:
+        raise ValueError("expected [R, C] or [G, R, C]")
+    if not Gs.is_contiguous():
+        raise ValueError("input must be contiguous")
+    nb, R, C = Gs.shape
+    odt = Gs.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((nb, R, C), dtype=odt, device=Gs.device)
+    else:
+        if out.shape != (nb, R, C) and out.shape != (R, C):
+            raise ValueError("out has the wrong shape")
+        if not out.is_contiguous() or out.device != Gs.device:
+            raise ValueError("out must be contiguous on the input's device")
+        odt = out.dtype
+    p, _keep = make_params(steps, coeffs, mode, restart_after, safety, eps, compute_dtype)
+    need = ctypes.c_size_t(0)
+    _check(lib().ns_workspace_size(nb, R, C, ctypes.byref(p), ctypes.byref(need)), "ns_workspace_size")
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(1, need.value), dtype=torch.uint8, device=Gs.device)
+    if status is not None and (status.dtype != torch.int32 or status.numel() < nb or not status.is_cuda):
+        raise ValueError("status must be an int32 CUDA tensor with G entries")
+    with torch.cuda.device(Gs.device):
+        code = lib().ns_orthogonalize(
+            ctypes.c_void_p(Gs.data_ptr()), _dtype_code(Gs.dtype),
+            ctypes.c_void_p(out.data_ptr()), _dtype_code(odt),
+            nb, R, C, ctypes.byref(p),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+            ctypes.c_void_p(status.data_ptr()) if status is not None else None,
+            ctypes.c_void_p(_stream_handle(Gs.device)))
+    _check(code, "ns_orthogonalize")
+    return out[0] if (squeeze and out.dim() == 3) else out
+
+
+def timing_enable(on: bool = True):
+    _check(lib().ns_timing_enable(1 if on else 0), "ns_timing_enable")
+
+
+def timing_collect(max_entries: int = 1 << 16):
+    """[(kernel name, ms), ...] for every launch recorded since the last collect."""
+    kinds = (ctypes.c_int32 * max_entries)()
+    ms = (ctypes.c_float * max_entries)()
+    n = ctypes.c_int32(0)
+    _check(lib().ns_timing_collect(kinds, ms, max_entries, ctypes.byref(n)), "ns_timing_collect")
+    return [(KIND_NAMES[kinds[i]], float(ms[i])) for i in range(min(n.value, max_entries))]
+
+
+def copy(src: torch.Tensor, dst: torch.Tensor):
+    """Library copy kernel (byte-counter calibration)."""
+    nbytes = src.numel() * src.element_size()
+    with torch.cuda.device(src.device):
+        _check(lib().nsg_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                              ctypes.c_void_p(_stream_handle(src.device))), "nsg_copy")
+
+
+def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 0.0,
+            Cin: Optional[torch.Tensor] = None, symmetric: bool = False, transposed_out: bool = False,
+            diag: Optional[float] = None):
+    """Library GEMM building block: V = alpha A B^T + beta Cin over a batch.
+
+    A [b, M, K], B [b, N, K] (M, N, K multiples of 256) in one dtype.
+    Returns (V, V^T or None, V + diag I or None)."""
+    b, M, K = A.shape
+    N = B.shape[1]
+    out = torch.empty((b, M, N), dtype=A.dtype, device=A.device)
+    out_t = torch.empty((b, N, M), dtype=A.dtype, device=A.device) if transposed_out else None
+    out_d = torch.empty((b, M, N), dtype=A.dtype, device=A.device) if diag is not None else None
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    with torch.cuda.device(A.device):
+        code = lib().nsg_gemm_nt(_dtype_code(A.dtype), 1 if symmetric else 0, b, M, N, K,
+                                 ptr(A), K, ptr(B), K, float(alpha), float(beta), ptr(Cin), N,
+                                 ptr(out), N, ptr(out_t), M, ptr(out_d), float(diag or 0.0),
+                                 ctypes.c_void_p(_stream_handle(A.device)))
+    _check(code, "nsg_gemm_nt")
+    return out, out_t, out_d

@@ -1,0 +1,586 @@
+// Host runtime of libnsg: argument validation, the bucket planner (transpose,
+// mode, tile configuration, workspace layout, launch list, FLOP tally) and the
+// sequencer that enqueues the standard or Gram Newton–Schulz launches.
+//
+// The launch lists follow the Dion3 paper: Algorithm 1 (standard NS) and
+// Algorithm 3 (stabilized Gram NS, with the a*I terms moved into fp32
+// epilogues as in Appendix B.2.3).  Square matrices run Algorithm 1 in "gram"
+// mode (Section 4.1, last paragraph).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "nsg.h"
+#include "nsg_internal.h"
+
+namespace nsg {
+namespace {
+
+const double kMuon[3] = {3.4445, -4.7750, 2.0315};  // "muon" kernel card, "How it works"
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+size_t dtype_size(int dt) { return dt == NSG_F32 ? 4 : 2; }
+bool valid_dtype(int dt) { return dt == NSG_F16 || dt == NSG_BF16 || dt == NSG_F32; }
+
+// Workspace buffers, each [G][rows][cols] in the compute dtype unless noted.
+enum Buf : int {
+  kPartials = 0,  // fp32 [G][nchunks]
+  kGScale,        // fp32 [G]
+  kX0,            // np x mp   (X0 scaled by 2^e)
+  kX0T,           // mp x np
+  kX1,            // np x mp   (X after the restart / standard ping-pong)
+  kX1T,           // mp x np
+  kS0, kS1, kS2, kS3, kS4, kS5,  // np x np
+  kNumBufs
+};
+
+struct Launch {
+  int kind = 0;  // 0 reduce, 1 scale, 2 gen GEMM, 3 sym GEMM
+  int step = 0;
+  std::string label;
+  int A = kNone, B = kNone, Cin = kNone, out0 = kNone, out1 = kNone, out2 = kNone;
+  int M = 0, N = 0, K = 0, Mv = 0, Nv = 0;
+  float alpha = 1.f, beta = 0.f, diag = 0.f;
+  int gpow = 0;
+  bool final_out = false;
+  double flops = 0.0, bytes = 0.0;
+};
+
+struct Plan {
+  int64_t R = 0, C = 0, n = 0, m = 0, np = 0, mp = 0;
+  bool tr = false;
+  bool gram = false;
+  int T = 0, restart = 0;  // restart at the top of step `restart` (0: none)
+  int cdtype = NSG_F16;
+  int cfg = kTile128;
+  int fexp = 0;
+  int nchunks = 0;
+  std::vector<double> a, b, c;
+  std::vector<Launch> launches;
+  // workspace layout: per-buffer byte offset and per-matrix element stride
+  size_t off[kNumBufs] = {0};
+  int64_t rows[kNumBufs] = {0}, cols[kNumBufs] = {0};
+  bool used[kNumBufs] = {false};
+  size_t total = 0;
+};
+
+nsg_status_t validate_params(const nsg_params_t *p) {
+  if (p == nullptr) return NSG_ERR_INVALID_ARG;
+  if (p->steps < 1 || p->steps > NSG_MAX_STEPS) return NSG_ERR_INVALID_ARG;
+  if (p->coeffs == nullptr) return NSG_ERR_INVALID_ARG;
+  if (p->n_coeffs != 3 && p->n_coeffs != 3 * p->steps) return NSG_ERR_INVALID_ARG;
+  for (int i = 0; i < p->n_coeffs; ++i)
+    if (!std::isfinite(p->coeffs[i])) return NSG_ERR_INVALID_ARG;
+  if (p->mode != NSG_STANDARD && p->mode != NSG_GRAM) return NSG_ERR_INVALID_ARG;
+  if (p->restart_after < 0) return NSG_ERR_INVALID_ARG;
+  if (!(p->safety > 0.f) || !std::isfinite(p->safety)) return NSG_ERR_INVALID_ARG;
+  if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return NSG_ERR_INVALID_ARG;
+  if (!valid_dtype(p->compute_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  return NSG_OK;
+}
+
+nsg_status_t validate_shape(int64_t G, int64_t R, int64_t C) {
+  if (G < 0 || R < 0 || C < 0) return NSG_ERR_SHAPE;
+  if (R > NSG_MAX_SIDE || C > NSG_MAX_SIDE || G > 65535) return NSG_ERR_SHAPE;
+  return NSG_OK;
+}
+
+// Tile configuration from (n, m, dtype) only — never from G — so a matrix's
+// arithmetic is the same in any bucket.
+int choose_cfg(int64_t np, int64_t mp, int dt) {
+  (void)mp;
+  (void)dt;
+  (void)np;
+  return kTile128;
+}
+
+double sym_tiles(int64_t M, int bm) {
+  const double t = (double)(M / bm);
+  return t * (t + 1.0) / 2.0;
+}
+
+void add_gemm(Plan &P, bool sym, int step, const char *label, int A, int B, int Cin, int out0,
+              int out1, int out2, int64_t M, int64_t N, int64_t K, int64_t Mv, int64_t Nv, double alpha,
+              double beta, double diag, int gpow, bool final_out) {
+  Launch L;
+  L.kind = sym ? 3 : 2;
+  L.step = step;
+  L.label = label;
+  L.A = A; L.B = B; L.Cin = Cin; L.out0 = out0; L.out1 = out1; L.out2 = out2;
+  L.M = (int)M; L.N = (int)N; L.K = (int)K; L.Mv = (int)Mv; L.Nv = (int)Nv;
+  L.alpha = (float)alpha; L.beta = (float)beta; L.diag = (float)diag;
+  L.gpow = gpow;
+  L.final_out = final_out;
+  const int bm = tile_m(P.cfg);
+  L.flops = sym ? 2.0 * sym_tiles(M, bm) * bm * bm * (double)K : 2.0 * (double)M * N * K;
+  // algorithmic bytes: valid operands read once, valid outputs written once
+  const double es = (double)dtype_size(P.cdtype);
+  // valid K: K of a GEMM over X's long side is m, else n
+  const double Kv = (K == P.mp) ? (double)P.m : (double)P.n;
+  double bytes = es * ((double)Mv * Kv + (double)Nv * Kv);
+  if (Cin != kNone) bytes += es * (double)Mv * Nv;
+  int outs = (out0 != kNone) + (out1 != kNone) + (out2 != kNone);
+  bytes += es * outs * (double)Mv * Nv;
+  L.bytes = bytes;
+  for (int id : {A, B, Cin, out0, out1, out2})
+    if (id >= 0) P.used[id] = true;
+  P.launches.push_back(L);
+}
+
+nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, int out_dtype, Plan &P) {
+  P.R = R; P.C = C;
+  P.tr = R > C;
+  P.n = std::min(R, C);
+  P.m = std::max(R, C);
+  P.np = round_up(P.n, kPad);
+  P.mp = round_up(P.m, kPad);
+  P.T = p->steps;
+  P.cdtype = p->compute_dtype;
+  P.gram = (p->mode == NSG_GRAM) && (P.n < P.m);
+  P.restart = (P.gram && p->restart_after >= 1 && p->restart_after < P.T) ? p->restart_after + 1 : 0;
+  P.cfg = choose_cfg(P.np, P.mp, P.cdtype);
+  // power-of-two range shift f ~ log2(sqrt(n)): keeps X0 = X/||X||_F and
+  // R0 = X0 X0^T away from fp16 subnormals (X0 entries ~ 1/sqrt(nm)).
+  P.fexp = (int)std::floor(std::log2((double)P.n) / 2.0);
+  if (P.fexp < 0) P.fexp = 0;
+  P.nchunks = (int)((R * C + kNormChunk - 1) / kNormChunk);
+  P.a.resize(P.T); P.b.resize(P.T); P.c.resize(P.T);
+  for (int t = 0; t < P.T; ++t) {
+    const double *cc = (p->n_coeffs == 3) ? p->coeffs : p->coeffs + 3 * t;
+    P.a[t] = cc[0]; P.b[t] = cc[1]; P.c[t] = cc[2];
+  }
+  const int64_t np = P.np, mp = P.mp, n = P.n, m = P.m;
+  const double two_f = std::ldexp(1.0, P.fexp);  // 2^f
+  const double xs0 = 1.0 / two_f;                  // X0 = r 2^-f X_stored
+
+  for (int i = 0; i < kNumBufs; ++i) { P.rows[i] = 0; P.cols[i] = 0; P.used[i] = false; }
+  P.rows[kX0] = np; P.cols[kX0] = mp;
+  P.rows[kX0T] = mp; P.cols[kX0T] = np;
+  P.rows[kX1] = np; P.cols[kX1] = mp;
+  P.rows[kX1T] = mp; P.cols[kX1T] = np;
+  for (int i = kS0; i <= kS5; ++i) { P.rows[i] = np; P.cols[i] = np; }
+  P.used[kPartials] = P.used[kGScale] = true;
+
+  {
+    Launch L; L.kind = 0; L.label = "norm_reduce"; L.bytes = (double)R * C * dtype_size(0); P.launches.push_back(L);
+    Launch S; S.kind = 1; S.label = "scale_cast_T"; S.bytes = 0; P.launches.push_back(S);
+  }
+  P.used[kX0] = P.used[kX0T] = true;
+  const int last = P.T + 1;
+  const int OUT = kOutUser;
+
+  if (!P.gram) {
+    // Algorithm 1: A = X X^T ; B = b A + c A^2 ; X = a X + B X.
+    int X = kX0, XT = kX0T, Xn = kX1, XnT = kX1T;
+    double xs = xs0;
+    int xpow = 1;
+    for (int t = 1; t <= P.T; ++t) {
+      const double a = P.a[t - 1], b = P.b[t - 1], c = P.c[t - 1];
+      // A_true = xs^2 r^(2 xpow) X_s X_s^T; stored A~ = A_true / xs^2
+      add_gemm(P, true, t, "A=XXt", X, X, kNone, kS0, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
+               2 * xpow, false);
+      const double as = xs * xs;
+      add_gemm(P, true, t, "B=bA+cA2", kS0, kS0, kS0, kS1, kNone, kNone, np, np, np, n, n, c * as * as,
+               b * as, 0.0, 0, false);
+      if (t < P.T) {
+        add_gemm(P, false, t, "X=aX+BX", kS1, XT, X, Xn, XnT, kNone, np, mp, np, n, m, xs, a * xs, 0.0,
+                 xpow, false);
+        std::swap(X, Xn);
+        std::swap(XT, XnT);
+      } else if (P.tr) {
+        // X'^T = a X^T + X^T B (B exactly symmetric): NT with A = X^T, B = B
+        add_gemm(P, false, last, "Yt=aXt+XtB", XT, kS1, XT, OUT, kNone, kNone, mp, np, np, m, n, xs,
+                 a * xs, 0.0, xpow, true);
+      } else {
+        add_gemm(P, false, last, "Y=aX+BX", kS1, XT, X, OUT, kNone, kNone, np, mp, np, n, m, xs, a * xs,
+                 0.0, xpow, true);
+      }
+      xs = 1.0;
+      xpow = 0;
+    }
+  } else {
+    // Algorithm 3 with the implicit a*I form of Appendix B.2.3.
+    int Xb = kX0, XbT = kX0T;
+    double xs = xs0;
+    int xpow = 1;
+    int Rb = kS0, Zb = kS1, Qcur = kNone, Qfree[2] = {kS2, kS3}, RZb = kS4, RZTb = kS5;
+    bool r_scaled = true;  // R_true = 2^-2f R_stored (only R0)
+    add_gemm(P, true, 0, "R0=XXt", kX0, kX0, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
+             false);
+    for (int t = 1; t <= P.T; ++t) {
+      const double a = P.a[t - 1], b = P.b[t - 1], c = P.c[t - 1];
+      if (t == P.restart) {
+        // X <- Q X ; R <- X X^T ; Q <- I   (Alg. 3, "restart to stabilize")
+        add_gemm(P, false, t, "X=QX", Qcur, XbT, kNone, kX1, kX1T, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
+                 xpow, false);
+        Xb = kX1; XbT = kX1T; xs = 1.0; xpow = 0;
+        add_gemm(P, true, t, "R=XXt", kX1, kX1, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
+                 0, false);
+        r_scaled = false;
+        Qcur = kNone;
+      }
+      const double rs = r_scaled ? 1.0 / (two_f * two_f) : 1.0;
+      // Z = b R + c R^2 ; with Q = I the new Q = Z + a I comes from the same
+      // fp32 accumulator (second store).
+      const int qnew = (Qcur == kNone) ? Qfree[0] : kNone;
+      add_gemm(P, true, t, qnew != kNone ? "Z (+Q=Z+aI)" : "Z=bR+cR2", Rb, Rb, Rb, Zb, kNone, qnew, np, np,
+               np, n, n, c * rs * rs, b * rs, a, 0, false);
+      if (Qcur == kNone) {
+        Qcur = Qfree[0];
+      } else {
+        const int qn = (Qcur == Qfree[0]) ? Qfree[1] : Qfree[0];
+        add_gemm(P, false, t, "Q=QZ+aQ", Qcur, Zb, Qcur, qn, kNone, kNone, np, np, np, n, n, 1.0, a, 0.0, 0,
+                 false);
+        Qcur = qn;
+      }
+      const bool need_r = (t < P.T) && (t + 1 != P.restart);
+      if (need_r) {
+        // RZ = R Z + a R (stored with R's scale), also written transposed
+        add_gemm(P, false, t, "RZ=RZ+aR", Rb, Zb, Rb, RZb, RZTb, kNone, np, np, np, n, n, 1.0, a, 0.0, 0,
+                 false);
+        // R = Z RZ + a RZ : NT with B = RZ^T
+        add_gemm(P, true, t, "R=Z.RZ+aRZ", Zb, RZTb, RZb, Rb, kNone, kNone, np, np, np, n, n, rs, a * rs,
+                 0.0, 0, false);
+        r_scaled = false;
+      }
+    }
+    if (P.tr) {
+      // Y^T = X^T Q^T : NT with A = X^T (m x n), B = Q
+      add_gemm(P, false, last, "Yt=XtQt", XbT, Qcur, kNone, OUT, kNone, kNone, mp, np, np, m, n, xs, 0.0,
+               0.0, xpow, true);
+    } else {
+      add_gemm(P, false, last, "Y=QX", Qcur, XbT, kNone, OUT, kNone, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
+               xpow, true);
+    }
+  }
+  P.launches[1].bytes = (double)R * C * dtype_size(0) + 2.0 * (double)n * m * dtype_size(P.cdtype);
+
+  // workspace layout
+  size_t off = 0;
+  for (int i = 0; i < kNumBufs; ++i) {
+    if (!P.used[i]) { P.off[i] = 0; continue; }
+    size_t per;
+    if (i == kPartials) per = (size_t)P.nchunks * 4;
+    else if (i == kGScale) per = 4;
+    else per = (size_t)P.rows[i] * P.cols[i] * dtype_size(P.cdtype);
+    P.off[i] = off;
+    off = align_up(off + per * (size_t)G, NSG_WORKSPACE_ALIGN);
+  }
+  P.total = off;
+  (void)out_dtype;
+  return NSG_OK;
+}
+
+int64_t elem_stride(const Plan &P, int id) {
+  if (id == kPartials) return P.nchunks;
+  if (id == kGScale) return 1;
+  return P.rows[id] * P.cols[id];
+}
+
+// ---- optional launch timing (process-global) ----
+struct TimingRec {
+  int kind;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+}  // namespace nsg
+
+using namespace nsg;
+
+extern "C" {
+
+void ns_default_params(nsg_params_t *p) {
+  if (p == nullptr) return;
+  p->steps = 5;
+  p->coeffs = kMuon;
+  p->n_coeffs = 3;
+  p->mode = NSG_GRAM;
+  p->restart_after = 2;
+  p->safety = 1.05f;
+  p->eps = 1e-7f;
+  p->compute_dtype = NSG_F16;
+}
+
+const char *ns_status_string(nsg_status_t s) {
+  switch (s) {
+    case NSG_OK: return "ok";
+    case NSG_ERR_INVALID_ARG: return "invalid argument";
+    case NSG_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case NSG_ERR_SHAPE: return "unsupported shape";
+    case NSG_ERR_WORKSPACE_TOO_SMALL: return "workspace missing, misaligned or too small";
+    case NSG_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+nsg_status_t ns_workspace_size(int64_t G, int64_t R, int64_t C, const nsg_params_t *p, size_t *bytes) {
+  if (bytes == nullptr) return NSG_ERR_INVALID_ARG;
+  nsg_status_t st = validate_params(p);
+  if (st != NSG_OK) return st;
+  st = validate_shape(G, R, C);
+  if (st != NSG_OK) return st;
+  if (G == 0 || R == 0 || C == 0) {
+    *bytes = 0;
+    return NSG_OK;
+  }
+  Plan P;
+  st = build_plan(R, C, p, G, NSG_F16, P);
+  if (st != NSG_OK) return st;
+  *bytes = P.total;
+  return NSG_OK;
+}
+
+nsg_status_t ns_flops(int64_t R, int64_t C, const nsg_params_t *p, double *credited, double *executed) {
+  nsg_status_t st = validate_params(p);
+  if (st != NSG_OK) return st;
+  st = validate_shape(1, R, C);
+  if (st != NSG_OK) return st;
+  if (R == 0 || C == 0) {
+    if (credited) *credited = 0.0;
+    if (executed) *executed = 0.0;
+    return NSG_OK;
+  }
+  Plan P;
+  st = build_plan(R, C, p, 1, NSG_F16, P);
+  if (st != NSG_OK) return st;
+  const double n = (double)P.n, m = (double)P.m, T = (double)P.T;
+  double cr;
+  if (!P.gram) {
+    cr = 2.0 * T * (2.0 * m * n * n + n * n * n);  // 2T(2 alpha + 1) n^3
+  } else {
+    cr = 4.0 * T * n * n * n + 3.0 * m * n * n - 3.0 * n * n * n;  // (4T + 3 alpha - 3) n^3
+    if (P.restart) cr += 3.0 * (m * n * n - n * n * n);            // + 3(alpha - 1) n^3
+  }
+  double ex = 0.0;
+  for (const Launch &L : P.launches) ex += L.flops;
+  if (credited) *credited = cr;
+  if (executed) *executed = ex;
+  return NSG_OK;
+}
+
+nsg_status_t ns_plan(int64_t R, int64_t C, const nsg_params_t *p, nsg_launch_info_t *entries,
+                     int32_t max_entries, int32_t *count) {
+  if (count == nullptr || max_entries < 0 || (max_entries > 0 && entries == nullptr)) return NSG_ERR_INVALID_ARG;
+  nsg_status_t st = validate_params(p);
+  if (st != NSG_OK) return st;
+  st = validate_shape(1, R, C);
+  if (st != NSG_OK) return st;
+  if (R == 0 || C == 0) {
+    *count = 0;
+    return NSG_OK;
+  }
+  Plan P;
+  st = build_plan(R, C, p, 1, NSG_F16, P);
+  if (st != NSG_OK) return st;
+  *count = (int32_t)P.launches.size();
+  for (int i = 0; i < (int)P.launches.size() && i < max_entries; ++i) {
+    const Launch &L = P.launches[i];
+    nsg_launch_info_t &e = entries[i];
+    e.kind = L.kind;
+    e.step = L.step;
+    e.M = L.Mv; e.N = L.Nv;
+    e.K = (L.kind >= 2) ? ((L.K == P.mp) ? P.m : P.n) : 0;
+    e.flops = L.flops;
+    e.bytes = L.bytes;
+    std::memset(e.label, 0, sizeof(e.label));
+    std::strncpy(e.label, L.label.c_str(), sizeof(e.label) - 1);
+  }
+  return NSG_OK;
+}
+
+nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32_t out_dtype, int64_t G,
+                              int64_t R, int64_t C, const nsg_params_t *p, void *workspace,
+                              size_t workspace_bytes, int32_t *status, void *stream) {
+  nsg_status_t st = validate_params(p);
+  if (st != NSG_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  st = validate_shape(G, R, C);
+  if (st != NSG_OK) return st;
+  if (G == 0 || R == 0 || C == 0) return NSG_OK;
+  if (in == nullptr || out == nullptr) return NSG_ERR_INVALID_ARG;
+  Plan P;
+  st = build_plan(R, C, p, G, out_dtype, P);
+  if (st != NSG_OK) return st;
+  if (workspace == nullptr || workspace_bytes < P.total ||
+      (reinterpret_cast<uintptr_t>(workspace) % NSG_WORKSPACE_ALIGN) != 0)
+    return NSG_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = reinterpret_cast<char *>(workspace);
+  auto ptr = [&](int id) -> void * { return id >= 0 ? ws + P.off[id] : nullptr; };
+  const size_t es = dtype_size(P.cdtype);
+  (void)es;
+
+  std::unique_lock<std::mutex> lk(g_tmu, std::defer_lock);
+  bool timing = false;
+  {
+    std::lock_guard<std::mutex> g(g_tmu);
+    timing = g_timing;
+  }
+
+  for (const Launch &L : P.launches) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (timing) {
+      std::lock_guard<std::mutex> g(g_tmu);
+      e0 = take_event();
+      e1 = take_event();
+      if (e0 && hipEventRecord(e0, s) != hipSuccess) return NSG_ERR_HIP;
+    }
+    hipError_t err = hipSuccess;
+    if (L.kind == 0) {
+      NormReduceArgs a;
+      a.in = in; a.in_dtype = in_dtype; a.elems = R * C; a.nchunks = P.nchunks;
+      a.partials = reinterpret_cast<float *>(ptr(kPartials));
+      a.batch = (int32_t)G;
+      err = launch_norm_reduce(a, s);
+    } else if (L.kind == 1) {
+      ScaleArgs a;
+      a.in = in; a.in_dtype = in_dtype; a.R = R; a.C = C;
+      a.partials = reinterpret_cast<const float *>(ptr(kPartials));
+      a.nchunks = P.nchunks;
+      a.safety = p->safety; a.eps = p->eps; a.fexp = P.fexp;
+      a.tr = P.tr ? 1 : 0;
+      a.rows_p = (int32_t)(P.tr ? P.mp : P.np);
+      a.cols_p = (int32_t)(P.tr ? P.np : P.mp);
+      a.same = P.tr ? ptr(kX0T) : ptr(kX0);
+      a.swap = P.tr ? ptr(kX0) : ptr(kX0T);
+      a.stride = P.np * P.mp;
+      a.cdtype = P.cdtype;
+      a.gscale = reinterpret_cast<float *>(ptr(kGScale));
+      a.status = status;
+      a.batch = (int32_t)G;
+      err = launch_scale(a, s);
+    } else {
+      GemmArgs a;
+      a.A = ptr(L.A); a.lda = P.cols[L.A]; a.sA = elem_stride(P, L.A);
+      a.B = ptr(L.B); a.ldb = P.cols[L.B]; a.sB = elem_stride(P, L.B);
+      if (L.Cin >= 0) { a.Cin = ptr(L.Cin); a.ldc = P.cols[L.Cin]; a.sC = elem_stride(P, L.Cin); }
+      if (L.out0 == kOutUser) {
+        a.out0 = out;
+        a.ld0 = C;  // the caller's [R, C] layout; final launches produce exactly that
+        a.s0 = R * C;
+        a.out0_dtype = out_dtype;
+        a.out0_pad = 0;
+        a.status = status;
+      } else if (L.out0 >= 0) {
+        a.out0 = ptr(L.out0); a.ld0 = P.cols[L.out0]; a.s0 = elem_stride(P, L.out0);
+        a.out0_dtype = P.cdtype; a.out0_pad = 1;
+      }
+      if (L.out1 >= 0) { a.out1 = ptr(L.out1); a.ld1 = P.cols[L.out1]; a.s1 = elem_stride(P, L.out1); }
+      if (L.out2 >= 0) { a.out2 = ptr(L.out2); a.ld2 = P.cols[L.out2]; a.s2 = elem_stride(P, L.out2); }
+      a.diag = L.diag;
+      a.M = L.M; a.N = L.N; a.K = L.K; a.Mv = L.Mv; a.Nv = L.Nv;
+      a.alpha = L.alpha; a.beta = L.beta;
+      a.gscale = reinterpret_cast<const float *>(ptr(kGScale));
+      a.gpow = L.gpow;
+      a.batch = (int32_t)G;
+      err = launch_gemm(P.cdtype, L.kind == 3, P.cfg, a, s);
+    }
+    if (err != hipSuccess) return NSG_ERR_HIP;
+    if (timing) {
+      std::lock_guard<std::mutex> g(g_tmu);
+      if (e1 && hipEventRecord(e1, s) != hipSuccess) return NSG_ERR_HIP;
+      if (e0 && e1) g_recs.push_back({L.kind, e0, e1});
+    }
+  }
+  return NSG_OK;
+}
+
+nsg_status_t ns_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> g(g_tmu);
+  g_timing = on != 0;
+  for (auto &r : g_recs) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_recs.clear();
+  return NSG_OK;
+}
+
+nsg_status_t ns_timing_collect(int32_t *kinds, float *ms, int32_t max_entries, int32_t *count) {
+  if (count == nullptr || max_entries < 0) return NSG_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_tmu);
+  nsg_status_t st = NSG_OK;
+  int i = 0;
+  for (auto &r : g_recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) st = NSG_ERR_HIP;
+    float t = 0.f;
+    if (st == NSG_OK && hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) st = NSG_ERR_HIP;
+    if (i < max_entries) {
+      if (kinds) kinds[i] = r.kind;
+      if (ms) ms[i] = t;
+    }
+    ++i;
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  *count = i;
+  g_recs.clear();
+  return st;
+}
+
+nsg_status_t nsg_copy(const void *src, void *dst, size_t bytes, void *stream) {
+  if (bytes == 0) return NSG_OK;
+  if (src == nullptr || dst == nullptr || bytes % 16 != 0) return NSG_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0) return NSG_ERR_INVALID_ARG;
+  return launch_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? NSG_OK : NSG_ERR_HIP;
+}
+
+nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda, const void *B, int64_t ldb, float alpha, float beta,
+                         const void *Cin, int64_t ldc, void *out, int64_t ldo, void *out_t, int64_t ldt,
+                         void *out_d, float diag, void *stream) {
+  if (!valid_dtype(dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (batch < 0 || M < 0 || N < 0 || K < 0) return NSG_ERR_SHAPE;
+  if (batch == 0 || M == 0 || N == 0) return NSG_OK;
+  if (M % kPad || N % kPad || K % kPad || K == 0 || batch > 65535 || M > NSG_MAX_SIDE || N > NSG_MAX_SIDE ||
+      K > NSG_MAX_SIDE)
+    return NSG_ERR_SHAPE;
+  if (A == nullptr || B == nullptr) return NSG_ERR_INVALID_ARG;
+  if (lda < K || ldb < K) return NSG_ERR_SHAPE;
+  if (symmetric && (M != N || out_t != nullptr)) return NSG_ERR_INVALID_ARG;
+  if (!symmetric && out_d != nullptr) return NSG_ERR_INVALID_ARG;
+  if (Cin != nullptr && ldc < N) return NSG_ERR_SHAPE;
+  if ((out != nullptr || out_d != nullptr) && ldo < N) return NSG_ERR_SHAPE;
+  if (out_t != nullptr && ldt < M) return NSG_ERR_SHAPE;
+  const size_t es = dtype_size(dtype);
+  if ((lda * (int64_t)es) % 16 || (ldb * (int64_t)es) % 16) return NSG_ERR_SHAPE;
+  GemmArgs a;
+  a.A = A; a.lda = lda; a.sA = M * lda;
+  a.B = B; a.ldb = ldb; a.sB = N * ldb;
+  if (Cin) { a.Cin = Cin; a.ldc = ldc; a.sC = M * ldc; }
+  a.out0 = out; a.ld0 = ldo; a.s0 = M * ldo; a.out0_dtype = dtype; a.out0_pad = 1;
+  if (out_t) { a.out1 = out_t; a.ld1 = ldt; a.s1 = N * ldt; }
+  if (out_d) { a.out2 = out_d; a.ld2 = ldo; a.s2 = M * ldo; a.diag = diag; }
+  a.M = (int32_t)M; a.N = (int32_t)N; a.K = (int32_t)K; a.Mv = (int32_t)M; a.Nv = (int32_t)N;
+  a.alpha = alpha; a.beta = beta;
+  a.batch = (int32_t)batch;
+  const int cfg = choose_cfg(M, N, dtype);
+  return launch_gemm(dtype, symmetric != 0, cfg, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? NSG_OK
+             : NSG_ERR_HIP;
+}
+
+}  // extern "C"

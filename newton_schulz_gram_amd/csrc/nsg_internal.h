@@ -1,0 +1,98 @@
+// Internal interface between the host runtime (nsg_api.cpp) and the gfx950
+// kernels (nsg_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "nsg.h"
+
+namespace nsg {
+
+// Every matrix the library keeps in its workspace has both dimensions padded
+// to a multiple of kPad, with zeros in the padding, so that GEMM tiles and
+// K-steps never need bounds checks on their loads.
+constexpr int kPad = 256;
+// Elements of the input summed by one block of the norm reduction.  Fixed, so
+// the reduction order of a matrix never depends on the bucket size.
+constexpr int64_t kNormChunk = 16384;
+
+enum BufferKind : int { kOutUser = -2, kNone = -1 };
+
+// One batched GEMM launch: V = alpha' A B^T + beta' Cin, with
+// alpha' = alpha * gscale[b]^gpow and beta' = beta * gscale[b]^gpow.
+// A is M x K (lda), B is N x K (ldb), Cin is M x N (ldc), all in the compute
+// dtype, batches `s*` elements apart.  M, N, K are padded sizes (multiples of
+// the tile); Mv x Nv is the valid corner.
+struct GemmArgs {
+  const void *A = nullptr;
+  int64_t lda = 0, sA = 0;
+  const void *B = nullptr;
+  int64_t ldb = 0, sB = 0;
+  const void *Cin = nullptr;
+  int64_t ldc = 0, sC = 0;
+  // out0: V (row-major, mirrored for symmetric launches).  Its dtype may be
+  // the caller's output dtype.  out0_pad = 1 writes zeros outside the valid
+  // corner (workspace outputs); 0 writes nothing there (the caller's buffer).
+  void *out0 = nullptr;
+  int64_t ld0 = 0, s0 = 0;
+  int32_t out0_dtype = NSG_F16;
+  int32_t out0_pad = 1;
+  // out1: V^T (general launches only), compute dtype, zero padding.
+  void *out1 = nullptr;
+  int64_t ld1 = 0, s1 = 0;
+  // out2: V + diag * I (symmetric launches only, mirrored), compute dtype.
+  void *out2 = nullptr;
+  int64_t ld2 = 0, s2 = 0;
+  float diag = 0.f;
+  int32_t M = 0, N = 0, K = 0;
+  int32_t Mv = 0, Nv = 0;
+  float alpha = 1.f, beta = 0.f;
+  const float *gscale = nullptr;
+  int32_t gpow = 0;
+  int32_t *status = nullptr;  // set to 1 for a batch with a non-finite out0 value
+  int32_t batch = 0;
+};
+
+struct NormReduceArgs {
+  const void *in = nullptr;
+  int32_t in_dtype = NSG_F16;
+  int64_t elems = 0;  // R * C
+  int32_t nchunks = 0;
+  float *partials = nullptr;  // [G][nchunks]
+  int32_t batch = 0;
+};
+
+// X_stored = RNE(G * 2^e) where kappa 2^f = r 2^e, kappa = 1/(s(nu+eps)),
+// r in [0.5, 1); so X0 = r 2^-f X_stored, and gscale[b] = r.
+struct ScaleArgs {
+  const void *in = nullptr;
+  int32_t in_dtype = NSG_F16;
+  int64_t R = 0, C = 0;
+  const float *partials = nullptr;
+  int32_t nchunks = 0;
+  float safety = 1.f, eps = 1e-7f;
+  int32_t fexp = 0;
+  int32_t tr = 0;  // 1: input is m x n (R > C)
+  int32_t rows_p = 0, cols_p = 0;  // padded dims of the input's own layout
+  void *same = nullptr;  // rows_p x cols_p, the input's layout
+  void *swap = nullptr;  // cols_p x rows_p, transposed
+  int64_t stride = 0;    // rows_p * cols_p elements per matrix in same/swap
+  int32_t cdtype = NSG_F16;
+  float *gscale = nullptr;
+  int32_t *status = nullptr;
+  int32_t batch = 0;
+};
+
+// Tile configurations of the GEMM kernels.
+enum TileCfg : int { kTile128 = 0, kTile256 = 1 };
+int tile_m(int cfg);
+
+hipError_t launch_gemm(int dtype, bool symmetric, int cfg, const GemmArgs &a, hipStream_t s);
+hipError_t launch_norm_reduce(const NormReduceArgs &a, hipStream_t s);
+hipError_t launch_scale(const ScaleArgs &a, hipStream_t s);
+hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
+
+}  // namespace nsg

@@ -1,0 +1,75 @@
+"""GPU tests of the GEMM building block (nsg_gemm_nt) against a plain fp32
+reference of the same product, through the C ABI."""
+import pytest
+import torch
+
+import newton_schulz_gram_amd as nsg
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float16: 2e-3, torch.bfloat16: 1.2e-2, torch.float32: 2e-6}
+
+
+def ref_nt(A, B, alpha=1.0, beta=0.0, Cin=None):
+    a = A.float().contiguous()
+    bt = B.float().transpose(1, 2).contiguous()
+    v = alpha * torch.bmm(a, bt)
+    if Cin is not None:
+        v = v + beta * Cin.float()
+    return v
+
+
+def rel(x, y):
+    return float((x.float() - y.float()).norm() / y.float().norm().clamp_min(1e-30))
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("MNK", [(256, 256, 256), (512, 768, 256), (256, 512, 1024)])
+def test_general_gemm(dtype, MNK):
+    M, N, K = MNK
+    g = torch.Generator(device="cuda").manual_seed(1)
+    A = torch.randn(3, M, K, device="cuda", generator=g).to(dtype)
+    B = torch.randn(3, N, K, device="cuda", generator=g).to(dtype)
+    Cin = torch.randn(3, M, N, device="cuda", generator=g).to(dtype)
+    out, out_t, _ = nsg.gemm_nt(A, B, alpha=0.5, beta=-1.25, Cin=Cin, transposed_out=True)
+    torch.cuda.synchronize()
+    ref = ref_nt(A, B, 0.5, -1.25, Cin)
+    assert rel(out, ref) <= TOL[dtype]
+    assert torch.equal(out_t, out.transpose(1, 2).contiguous())
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n,K", [(256, 512), (768, 256), (1024, 1024)])
+def test_symmetric_gemm_gram(dtype, n, K):
+    """X X^T on the lower-triangle tiles only, mirrored: exactly symmetric."""
+    g = torch.Generator(device="cuda").manual_seed(2)
+    X = torch.randn(2, n, K, device="cuda", generator=g).to(dtype)
+    out, _, _ = nsg.gemm_nt(X, X, alpha=2.0, symmetric=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out.transpose(1, 2))
+    assert rel(out, ref_nt(X, X, 2.0)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_symmetric_quadratic_with_dual_store(dtype):
+    """Z = b R + c R R^T (R symmetric) and the second store Z + a I."""
+    g = torch.Generator(device="cuda").manual_seed(3)
+    n = 512
+    X = torch.randn(1, n, 1024, device="cuda", generator=g) / 32
+    R = (X @ X.transpose(1, 2)).to(dtype)
+    R = ((R.float() + R.float().transpose(1, 2)) / 2).to(dtype)  # exactly symmetric
+    Z, _, Q = nsg.gemm_nt(R, R, alpha=2.0315, beta=-4.775, Cin=R, symmetric=True, diag=3.4445)
+    torch.cuda.synchronize()
+    ref = ref_nt(R, R, 2.0315, -4.775, R)
+    assert torch.equal(Z, Z.transpose(1, 2)) and torch.equal(Q, Q.transpose(1, 2))
+    assert rel(Z, ref) <= TOL[dtype]
+    eye = torch.eye(n, device="cuda", dtype=torch.bool).unsqueeze(0)
+    assert torch.equal(Q[~eye], Z[~eye])
+    refq = ref + 3.4445 * torch.eye(n, device="cuda")
+    assert rel(Q, refq) <= TOL[dtype]
+
+
+def test_gemm_rejects_unpadded_sizes():
+    A = torch.zeros(1, 200, 256, device="cuda", dtype=torch.float16)
+    with pytest.raises(nsg.NSGError):
+        nsg.gemm_nt(A, A)

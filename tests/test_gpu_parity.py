@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars: relative Frobenius error <= 3e-2 and cosine >= 0.97 per matrix for the
+fp16/bf16 paths, <= 1e-4 for the fp32 debug path; grouped and single-matrix
+outputs bitwise identical; repeated calls bitwise identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import newton_schulz_gram_amd as nsg
+import oracle
+import synth
+from synth import COEFFS_MUON, WORKLOADS
+from synth.workloads import conditioning_class_of, custom
+
+pytestmark = pytest.mark.gpu
+
+HALF_REL, HALF_COS, F32_REL = 3e-2, 0.97, 1e-4
+
+
+def metrics(out, ref):
+    """Per-matrix (relative Frobenius error, cosine) of out vs the fp64 ref."""
+    o = out.double().cpu().numpy().reshape(out.shape[0], -1)
+    r = np.asarray(ref, dtype=np.float64).reshape(o.shape[0], -1)
+    d = np.linalg.norm(o - r, axis=1)
+    rn = np.linalg.norm(r, axis=1)
+    on = np.linalg.norm(o, axis=1)
+    rel = d / np.maximum(rn, 1e-300)
+    cos = np.sum(o * r, axis=1) / np.maximum(on * rn, 1e-300)
+    return rel, cos
+
+
+def run(x, **kw):
+    y = nsg.orthogonalize(x.cuda(), **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_of(x, mode="gram", steps=5, coeffs=COEFFS_MUON, restart_after=2, safety=1.05):
+    return oracle.orthogonalize(x.double().numpy(), steps, coeffs, mode, restart_after, safety)
+
+
+def check(out, ref, compute, label=""):
+    rel, cos = metrics(out, ref)
+    if compute == "f32":
+        assert rel.max() <= F32_REL, (label, rel.max())
+    else:
+        assert rel.max() <= HALF_REL, (label, rel.max(), int(rel.argmax()))
+        assert cos.min() >= HALF_COS, (label, cos.min())
+    return rel, cos
+
+
+# ---------------------------------------------------------------------------
+# single fp32 128x512 matrix, both modes, fp32 and fp16 compute
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", ["gram", "standard"])
+@pytest.mark.parametrize("compute", ["f32", "f16", "bf16"])
+def test_single_128x512(mode, compute):
+    w = WORKLOADS["single_1x128x512_f32"]
+    x = synth.make(w)
+    ref = oracle_of(x, mode=mode, safety=1.0)
+    out = run(x, mode=mode, safety=1.0, compute_dtype=compute)
+    assert out.dtype == torch.float32
+    check(out, ref, compute, f"{mode}/{compute}")
+
+
+# ---------------------------------------------------------------------------
+# ragged and odd shapes, several tiles plus a tail
+# ---------------------------------------------------------------------------
+
+SHAPES = [(300, 1000), (1000, 300), (333, 333), (257, 513), (1, 50), (50, 1), (7, 9), (130, 4000),
+          (384, 768)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("mode", ["gram", "standard"])
+def test_ragged_shapes_fp16(shape, mode):
+    R, C = shape
+    x = custom(3, R, C, "f16", "gaussian", seed=21)
+    ref = oracle_of(x, mode=mode)
+    out = run(x, mode=mode)
+    assert out.shape == x.shape and out.dtype == torch.float16
+    check(out, ref, "f16", f"{shape}/{mode}")
+
+
+@pytest.mark.parametrize("shape", [(300, 1000), (1000, 300), (333, 333)])
+@pytest.mark.parametrize("compute", ["f32", "bf16"])
+def test_ragged_shapes_other_compute(shape, compute):
+    R, C = shape
+    x = custom(2, R, C, "f32", "gaussian", seed=22)
+    ref = oracle_of(x)
+    out = run(x, compute_dtype=compute)
+    check(out, ref, compute, f"{shape}/{compute}")
+
+
+@pytest.mark.parametrize("restart_after", [0, 1, 2, 3, 4, 5])
+def test_every_restart_location(restart_after):
+    x = custom(2, 256, 1024, "f16", "gaussian", seed=23)
+    ref = oracle_of(x, restart_after=restart_after)
+    out = run(x, restart_after=restart_after)
+    check(out, ref, "f16", f"restart {restart_after}")
+
+
+def test_per_step_coefficients_and_steps():
+    coeffs = [3.4445, -4.7750, 2.0315, 15 / 8, -10 / 8, 3 / 8, 2.0, -1.5, 0.5]
+    x = custom(2, 200, 600, "f16", "gaussian", seed=24)
+    for mode in ("gram", "standard"):
+        ref = oracle_of(x, mode=mode, steps=3, coeffs=coeffs, restart_after=1)
+        out = run(x, mode=mode, steps=3, coeffs=coeffs, restart_after=1, compute_dtype="f32")
+        check(out, ref, "f32", mode)
+
+
+# ---------------------------------------------------------------------------
+# GPT-2-small MLP bucket: 42 x 768x3072, seven conditionings
+# ---------------------------------------------------------------------------
+
+def test_gpt2s_bucket_all_conditionings():
+    w = WORKLOADS["gpt2s_mlp_42x768x3072_f16"]
+    x = synth.make(w)
+    ref = oracle_of(x, safety=w.safety)
+    out = run(x, safety=w.safety)
+    rel, cos = metrics(out, ref)
+    worst = {}
+    for g in range(w.G):
+        c = conditioning_class_of(w.G, g)
+        worst[c] = max(worst.get(c, 0.0), float(rel[g]))
+    print("per-class max rel error:", {k: round(v, 5) for k, v in worst.items()})
+    assert rel.max() <= HALF_REL, worst
+    assert cos.min() >= HALF_COS
+    # grouped == single, bitwise
+    for g in (0, 13, 41):
+        one = run(x[g:g + 1], safety=w.safety)
+        assert torch.equal(one[0], out[g])
+    # repeated call, bitwise
+    again = run(x, safety=w.safety)
+    assert torch.equal(again, out)
+
+
+# ---------------------------------------------------------------------------
+# MoE bucket: 512 x 2048x512 (transposed to 512 x 2048)
+# ---------------------------------------------------------------------------
+
+def test_moe_bucket_sampled():
+    w = WORKLOADS["moe_512x2048x512_f16"]
+    x = synth.make(w)
+    out = run(x, safety=w.safety)
+    idx = [0, 1, 77, 255, 300, 511]
+    ref = oracle_of(x[idx], safety=w.safety)
+    check(out[idx], ref, "f16", "moe")
+    for g in (0, 300):
+        one = run(x[g:g + 1], safety=w.safety)
+        assert torch.equal(one[0], out[g])
+
+
+# ---------------------------------------------------------------------------
+# Full-size buckets, sampled against the oracle
+# ---------------------------------------------------------------------------
+
+def test_llama7b_bucket_sampled():
+    w = WORKLOADS["llama7b_mlp_32x11008x4096_bf16"]
+    x = synth.make(w)
+    out = run(x, safety=w.safety)
+    assert out.dtype == torch.bfloat16 and out.shape == (32, 11008, 4096)
+    ref = oracle_of(x[:1], safety=w.safety)
+    rel, cos = check(out[:1], ref, "f16", "7b")
+    print("7b matrix 0: rel %.3e cos %.6f" % (rel[0], cos[0]))
+    one = run(x[5:6], safety=w.safety)
+    assert torch.equal(one[0], out[5])
+
+
+def test_square_bucket_standard_fallback_sampled():
+    w = WORKLOADS["square_32x4096x4096_f16"]
+    x = synth.make(w)
+    out = run(x, safety=w.safety)
+    ref = oracle_of(x[31:32], safety=w.safety)
+    rel, cos = check(out[31:32], ref, "f16", "square")
+    print("square matrix 31: rel %.3e cos %.6f" % (rel[0], cos[0]))
+
+
+# ---------------------------------------------------------------------------
+# Edge cases and API behaviour
+# ---------------------------------------------------------------------------
+
+def test_zero_matrix_and_status():
+    x = torch.zeros(2, 64, 256, dtype=torch.float16)
+    x[1] = torch.from_numpy(np.random.default_rng(0).standard_normal((64, 256))).half()
+    st = torch.full((2,), 7, dtype=torch.int32, device="cuda")
+    out = nsg.orthogonalize(x.cuda(), status=st)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0)
+    assert st.tolist() == [0, 0]
+
+
+def test_non_finite_input_sets_status():
+    x = torch.randn(3, 64, 256).half()
+    x[1, 3, 5] = float("inf")
+    st = torch.zeros(3, dtype=torch.int32, device="cuda")
+    out = nsg.orthogonalize(x.cuda(), status=st)
+    torch.cuda.synchronize()
+    assert st.tolist() == [0, 1, 0]
+    assert torch.isfinite(out[0]).all() and torch.isfinite(out[2]).all()
+
+
+def test_in_place_and_output_dtype():
+    x = custom(2, 200, 500, "f16", "gaussian", seed=31)
+    ref = oracle_of(x)
+    xc = x.cuda()
+    y32 = nsg.orthogonalize(xc, out_dtype=torch.float32)
+    y = nsg.orthogonalize(xc, out=xc)  # in place
+    torch.cuda.synchronize()
+    assert y.data_ptr() == xc.data_ptr()
+    check(y, ref, "f16")
+    check(y32, ref, "f16")
+    assert y32.dtype == torch.float32
+
+
+def test_empty_bucket():
+    x = torch.zeros(0, 16, 32, dtype=torch.float16, device="cuda")
+    assert nsg.orthogonalize(x).shape == (0, 16, 32)
+
+
+def test_single_matrix_2d_input():
+    x = custom(1, 100, 300, "bf16", "gaussian", seed=32)
+    out = nsg.orthogonalize(x[0].cuda())
+    torch.cuda.synchronize()
+    assert out.shape == (100, 300) and out.dtype == torch.bfloat16
+    check(out.unsqueeze(0), oracle_of(x), "f16")

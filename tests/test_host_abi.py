@@ -1,0 +1,149 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol include/nsg.h
+declares, validates arguments before touching the GPU, and its planner's FLOP
+tally matches the pages' formulas (no GPU needed for any of this)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import newton_schulz_gram_amd as nsg
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsg.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:nsg_status_t|void|const char \*)\s*\n?\s*(\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = nsg.lib()
+    names = header_functions()
+    assert len(names) >= 10, names
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(nsg.EXPORTS)
+
+
+def test_status_strings():
+    L = nsg.lib()
+    for code in range(6):
+        assert L.ns_status_string(code).decode() == nsg.STATUS[code]
+
+
+def test_default_params():
+    p = nsg.Params()
+    nsg.lib().ns_default_params(ctypes.byref(p))
+    assert p.steps == 5 and p.n_coeffs == 3 and p.mode == nsg.NSG_GRAM
+    assert p.restart_after == 2 and abs(p.safety - 1.05) < 1e-6 and abs(p.eps - 1e-7) < 1e-12
+    assert [p.coeffs[i] for i in range(3)] == list(nsg.MUON_COEFFS)
+    assert p.compute_dtype == nsg.NSG_F16
+
+
+def _call(G=2, R=64, C=128, in_dtype=0, out_dtype=0, ws_bytes=None, ws_ptr=1 << 20, **kw):
+    p, keep = nsg.make_params(**kw)
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    # fake device pointers: validation must fail before anything dereferences them
+    return nsg.lib().ns_orthogonalize(ctypes.c_void_p(0x1000), in_dtype, ctypes.c_void_p(0x2000), out_dtype,
+                                      G, R, C, ctypes.byref(p), ctypes.c_void_p(ws_ptr), ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(steps=0), 1),
+    (dict(steps=65), 1),
+    (dict(coeffs=[1.0, 2.0]), 1),
+    (dict(coeffs=[1.0, 2.0, float("nan")]), 1),
+    (dict(mode=7), 1),
+    (dict(restart_after=-1), 1),
+    (dict(safety=0.0), 1),
+    (dict(safety=float("inf")), 1),
+    (dict(eps=-1.0), 1),
+    (dict(compute_dtype=9), 2),
+    (dict(in_dtype=3), 2),
+    (dict(out_dtype=-1), 2),
+    (dict(G=-1), 3),
+    (dict(R=70000), 3),
+    (dict(ws_bytes=16), 4),
+    (dict(ws_ptr=(1 << 20) + 8), 4),
+])
+def test_validation_before_launch(kw, code):
+    assert _call(**kw) == code
+
+
+def test_empty_bucket_is_a_no_op():
+    assert _call(G=0) == 0
+    assert _call(R=0) == 0
+    assert _call(C=0) == 0
+    assert nsg.workspace_size(0, 10, 10) == 0
+
+
+def test_null_pointers_rejected():
+    p, keep = nsg.make_params()
+    L = nsg.lib()
+    assert L.ns_orthogonalize(None, 0, ctypes.c_void_p(0x2000), 0, 1, 8, 8, ctypes.byref(p),
+                              ctypes.c_void_p(1 << 20), 1 << 30, None, None) == 1
+    assert L.ns_orthogonalize(ctypes.c_void_p(0x1000), 0, ctypes.c_void_p(0x2000), 0, 1, 8, 8, None,
+                              ctypes.c_void_p(1 << 20), 1 << 30, None, None) == 1
+
+
+@pytest.mark.parametrize("R,C", [(128, 512), (768, 3072), (11008, 4096), (2048, 512), (300, 1000), (1000, 300)])
+def test_credited_flops_match_gram_formula(R, C):
+    n, m = min(R, C), max(R, C)
+    cr, ex = nsg.flops(R, C)
+    assert cr == pytest.approx(oracle.flops_gram_stable(n, m, 5), rel=1e-12)
+    assert ex >= 0.5 * cr
+
+
+@pytest.mark.parametrize("R,C", [(4096, 4096), (333, 333), (128, 512)])
+def test_credited_flops_standard(R, C):
+    n, m = min(R, C), max(R, C)
+    cr, _ = nsg.flops(R, C, mode="standard")
+    assert cr == pytest.approx(oracle.flops_standard(n, m, 5), rel=1e-12)
+
+
+def test_square_gram_falls_back_to_standard():
+    labels = [e["label"] for e in nsg.plan(4096, 4096, mode="gram")]
+    assert "R0=XXt" not in labels and labels.count("A=XXt") == 5
+    cr, _ = nsg.flops(4096, 4096, mode="gram")
+    assert cr == pytest.approx(oracle.flops_standard(4096, 4096, 5))
+
+
+def test_gram_plan_structure():
+    """Alg. 3: R0, then per step Z (+Q for a fresh Q), Q update, RZ and R; the
+    restart (X=QX, R=XX^T) at the top of step 3; R_2 and R_5 skipped; 18 GEMMs."""
+    P = nsg.plan(11008, 4096)
+    labels = [e["label"] for e in P]
+    gemms = [e for e in P if e["kernel"].startswith("gemm")]
+    assert len(gemms) == 18
+    assert labels[:3] == ["norm_reduce", "scale_cast_T", "R0=XXt"]
+    steps = {}
+    for e in P:
+        steps.setdefault(e["step"], []).append(e["label"])
+    assert steps[1] == ["Z (+Q=Z+aI)", "RZ=RZ+aR", "R=Z.RZ+aRZ"]
+    assert steps[2] == ["Z=bR+cR2", "Q=QZ+aQ"]
+    assert steps[3] == ["X=QX", "R=XXt", "Z (+Q=Z+aI)", "RZ=RZ+aR", "R=Z.RZ+aRZ"]
+    assert steps[5] == ["Z=bR+cR2", "Q=QZ+aQ"]
+    assert steps[6] == ["Yt=XtQt"]  # tall input: output written as Y^T, i.e. R x C
+    assert [e["label"] for e in nsg.plan(768, 3072)][-1] == "Y=QX"
+    # without a restart: Alg. 2 (with the implicit a I form)
+    labels0 = [e["label"] for e in nsg.plan(768, 3072, restart_after=0)]
+    assert "X=QX" not in labels0 and labels0.count("Q=QZ+aQ") == 4
+
+
+def test_executed_flops_sum_of_plan():
+    P = nsg.plan(768, 3072)
+    _, ex = nsg.flops(768, 3072)
+    assert ex == pytest.approx(sum(e["flops"] for e in P))
+
+
+def test_workspace_scales_with_bucket():
+    a = nsg.workspace_size(1, 11008, 4096)
+    b = nsg.workspace_size(32, 11008, 4096)
+    assert 31 * a <= b <= 32 * a + 32 * 256
+    assert a % 256 == 0 and b % 256 == 0
