@@ -1,0 +1,198 @@
+"""Benchmark: batched Gram Newton–Schulz on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one ns_orthogonalize call over the whole bucket (normalize, every
+GEMM of Algorithm 3 or 1, output), inputs resident in HBM.  Prints one JSON
+line: matrices/s (whole job), effective TFLOP/s from the pages' FLOP formula
+and its fraction of the fp16 dense MFMA peak, a roofline object for the
+dominant kernel (per-launch durations from HIP events recorded by the library
+on the stream its kernels run on), and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "matrices/s and effective TFLOP/s (% fp16 MFMA peak), Gram NS, 7B bucket"
+PEAK_FP16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "llama7b_mlp_32x11008x4096_bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("nsg_kernels.hip", "nsg_internal.h"):
+        with open(os.path.join(ROOT, "newton_schulz_gram_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_flops(entry, G):
+    """Pages' count for one launch over the bucket: 2 M N K for a general
+    product, M N K for a symmetric one (half the product is computed)."""
+    if entry["kernel"] == "gemm_nt":
+        return 2.0 * entry["M"] * entry["N"] * entry["K"] * G
+    if entry["kernel"] == "gemm_nt_sym":
+        return 1.0 * entry["M"] * entry["N"] * entry["K"] * G
+    return 0.0
+
+
+def cpu_baseline(w, x_cpu, budget_s: float = 30.0):
+    """The oracle as it stands, on a bounded sample: whole matrices of the bucket,
+    stopping once the time budget is spent (at least one matrix)."""
+    import numpy as np
+
+    import oracle
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads") or 0) for d in threadpool_info()) or None
+    except Exception:
+        pass
+    done, t0 = 0, time.perf_counter()
+    while done < w.G:
+        oracle.orthogonalize(x_cpu[done:done + 1].double().numpy(), w.steps, w.coeffs, w.mode,
+                             w.restart_after, w.safety)
+        done += 1
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "matrices/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{done} of {w.G} matrices ({w.R}x{w.C}), full NS in fp64 numpy, {dt:.1f} s",
+            "seconds_per_matrix": dt / done}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus > 1 is not supported "
+                                   "(matrices are independent: the bucket would be split across GPUs)"}))
+        sys.exit(2)
+
+    import torch
+
+    import newton_schulz_gram_amd as nsg
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    t_gen = time.perf_counter()
+    x_cpu = synth.make(w)
+    t_gen = time.perf_counter() - t_gen
+    x = x_cpu.to(dev)
+    out = torch.empty_like(x)
+    kw = dict(steps=w.steps, coeffs=w.coeffs, mode=w.mode, restart_after=w.restart_after,
+              safety=w.safety, compute_dtype=w.compute)
+    ws = torch.empty(nsg.workspace_size(w.G, w.R, w.C, **kw), dtype=torch.uint8, device=dev)
+    status = torch.zeros(w.G, dtype=torch.int32, device=dev)
+    plan = nsg.plan(w.R, w.C, **kw)
+    credited, executed = nsg.flops(w.R, w.C, **kw)
+
+    for _ in range(args.warmup):
+        nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
+    torch.cuda.synchronize()
+
+    nsg.timing_enable(True)
+    nsg.timing_collect()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recs = nsg.timing_collect()
+    nsg.timing_enable(False)
+
+    ms_per_step = 1e3 * wall / args.steps
+    value = w.G * args.steps / wall
+    eff_tflops = credited * w.G * args.steps / wall / 1e12
+
+    # per-launch durations, matched to the plan (same launch order every step)
+    per = len(plan)
+    assert len(recs) == per * args.steps, (len(recs), per, args.steps)
+    by_kernel = {}
+    for i, (name, ms) in enumerate(recs):
+        e = plan[i % per]
+        d = by_kernel.setdefault(name, {"ms": 0.0, "launches": 0, "algo_flops": 0.0, "bytes": 0.0})
+        d["ms"] += ms
+        d["launches"] += 1
+        d["algo_flops"] += algorithmic_flops(e, w.G)
+        d["bytes"] += e["bytes"] * w.G
+    dominant = max((k for k in by_kernel if k.startswith("gemm")), key=lambda k: by_kernel[k]["ms"])
+    d = by_kernel[dominant]
+    avg_ms = d["ms"] / d["launches"]
+    achieved = d["algo_flops"] / d["launches"] / (avg_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get(args.workload, {}).get(dominant)
+            if ent and ent.get("kernel_src") == kernel_source_hash():
+                traffic = ent.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
+                "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                "traffic": traffic, "avg_launch_ms": round(avg_ms, 4), "launches_per_step": d["launches"] // args.steps,
+                "algo_flops_per_launch": d["algo_flops"] / d["launches"]}
+    norm_ms = sum(by_kernel.get(k, {"ms": 0})["ms"] for k in ("norm_reduce", "scale_cast_transpose"))
+    norm_bytes = sum(by_kernel.get(k, {"bytes": 0})["bytes"] for k in ("norm_reduce", "scale_cast_transpose"))
+    kernels = {k: {"ms_per_step": round(v["ms"] / args.steps, 3),
+                   "tflops_algo": round(v["algo_flops"] / (v["ms"] * 1e-3) / 1e12, 1) if v["algo_flops"] else None}
+               for k, v in by_kernel.items()}
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if w.compute == "f16" else w.compute,
+        "data": "synthetic",
+        "config": {"workload": w.name, "G": w.G, "R": w.R, "C": w.C, "input_dtype": w.dtype,
+                   "mode": w.mode, "steps": w.steps, "restart_after": w.restart_after,
+                   "safety": w.safety, "coeffs": list(w.coeffs), "accumulate": "f32"},
+        "effective_tflops": round(eff_tflops, 2),
+        "pct_fp16_peak": round(100 * eff_tflops / PEAK_FP16_TFLOPS, 2),
+        "executed_tflops": round(executed * w.G * args.steps / wall / 1e12, 2),
+        "flops_per_matrix": {"credited": credited, "executed": executed},
+        "normalize_gbs": round(norm_bytes / (norm_ms * 1e-3) / 1e9, 1) if norm_ms else None,
+        "kernels": kernels,
+        "roofline": roofline,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "nonfinite_matrices": int(status.sum().item()),
+        "input_gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x_cpu, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -108,7 +108,8 @@ def test_per_step_coefficients_and_steps():
     x = custom(2, 200, 600, "f16", "gaussian", seed=24)
     for mode in ("gram", "standard"):
         ref = oracle_of(x, mode=mode, steps=3, coeffs=coeffs, restart_after=1)
-        out = run(x, mode=mode, steps=3, coeffs=coeffs, restart_after=1, compute_dtype="f32")
+        out = run(x, mode=mode, steps=3, coeffs=coeffs, restart_after=1, compute_dtype="f32",
+                  out_dtype=torch.float32)
         check(out, ref, "f32", mode)
 
 
