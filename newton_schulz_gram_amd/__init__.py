@@ -104,7 +104,7 @@ def lib() -> ctypes.CDLL:
     L.nsg_copy.argtypes = [vp, vp, sz, vp]
     L.nsg_copy.restype = i32
     L.nsg_gemm_nt.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp, i64, f32, f32, vp, i64,
-                              vp, i64, vp, i64, vp, f32, vp]
+                              vp, i64, vp, i64, vp, f32, i32, vp]
     L.nsg_gemm_nt.restype = i32
     _lib = L
     return L
@@ -244,10 +244,11 @@ def copy(src: torch.Tensor, dst: torch.Tensor):
 
 def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 0.0,
             Cin: Optional[torch.Tensor] = None, symmetric: bool = False, transposed_out: bool = False,
-            diag: Optional[float] = None):
+            diag: Optional[float] = None, tile: int = 0):
     """Library GEMM building block: V = alpha A B^T + beta Cin over a batch.
 
-    A [b, M, K], B [b, N, K] (M, N, K multiples of 256) in one dtype.
+    A [b, M, K], B [b, N, K] (M, N, K multiples of 256) in one dtype; tile 128
+    or 256 picks the kernel (0: the library's choice).
     Returns (V, V^T or None, V + diag I or None)."""
     b, M, K = A.shape
     N = B.shape[1]
@@ -258,7 +259,7 @@ def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 
     with torch.cuda.device(A.device):
         code = lib().nsg_gemm_nt(_dtype_code(A.dtype), 1 if symmetric else 0, b, M, N, K,
                                  ptr(A), K, ptr(B), K, float(alpha), float(beta), ptr(Cin), N,
-                                 ptr(out), N, ptr(out_t), M, ptr(out_d), float(diag or 0.0),
+                                 ptr(out), N, ptr(out_t), M, ptr(out_d), float(diag or 0.0), int(tile),
                                  ctypes.c_void_p(_stream_handle(A.device)))
     _check(code, "nsg_gemm_nt")
     return out, out_t, out_d

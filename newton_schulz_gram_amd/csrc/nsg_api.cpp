@@ -65,7 +65,8 @@ struct Plan {
   std::vector<Launch> launches;
   // workspace layout: per-buffer byte offset and per-matrix element stride
   size_t off[kNumBufs] = {0};
-  int64_t rows[kNumBufs] = {0}, cols[kNumBufs] = {0};
+  // rows x cols padded extent; ld = cols + skew (elements between rows)
+  int64_t rows[kNumBufs] = {0}, cols[kNumBufs] = {0}, ld[kNumBufs] = {0};
   bool used[kNumBufs] = {false};
   size_t total = 0;
 };
@@ -95,9 +96,8 @@ nsg_status_t validate_shape(int64_t G, int64_t R, int64_t C) {
 // arithmetic is the same in any bucket.
 int choose_cfg(int64_t np, int64_t mp, int dt) {
   (void)mp;
-  (void)dt;
-  (void)np;
-  return kTile128;
+  if (dt == NSG_F32) return kTile128;  // debug path
+  return np >= 512 ? kTile256 : kTile128;
 }
 
 double sym_tiles(int64_t M, int bm) {
@@ -159,12 +159,17 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
   const double two_f = std::ldexp(1.0, P.fexp);  // 2^f
   const double xs0 = 1.0 / two_f;                  // X0 = r 2^-f X_stored
 
-  for (int i = 0; i < kNumBufs; ++i) { P.rows[i] = 0; P.cols[i] = 0; P.used[i] = false; }
+  for (int i = 0; i < kNumBufs; ++i) { P.rows[i] = 0; P.cols[i] = 0; P.ld[i] = 0; P.used[i] = false; }
   P.rows[kX0] = np; P.cols[kX0] = mp;
   P.rows[kX0T] = mp; P.cols[kX0T] = np;
   P.rows[kX1] = np; P.cols[kX1] = mp;
   P.rows[kX1T] = mp; P.cols[kX1T] = np;
   for (int i = kS0; i <= kS5; ++i) { P.rows[i] = np; P.cols[i] = np; }
+  // Row pitch = padded width + 128 bytes: consecutive rows of an operand tile
+  // then start in different L2 channels (a pitch that is a multiple of 4 KB
+  // sends every row of a tile slice to the same channel).
+  const int64_t skew = 128 / (int64_t)dtype_size(P.cdtype);
+  for (int i = kX0; i < kNumBufs; ++i) P.ld[i] = P.cols[i] + skew;
   P.used[kPartials] = P.used[kGScale] = true;
 
   {
@@ -268,7 +273,7 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     size_t per;
     if (i == kPartials) per = (size_t)P.nchunks * 4;
     else if (i == kGScale) per = 4;
-    else per = (size_t)P.rows[i] * P.cols[i] * dtype_size(P.cdtype);
+    else per = (size_t)P.rows[i] * P.ld[i] * dtype_size(P.cdtype);
     P.off[i] = off;
     off = align_up(off + per * (size_t)G, NSG_WORKSPACE_ALIGN);
   }
@@ -280,7 +285,7 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
 int64_t elem_stride(const Plan &P, int id) {
   if (id == kPartials) return P.nchunks;
   if (id == kGScale) return 1;
-  return P.rows[id] * P.cols[id];
+  return P.rows[id] * P.ld[id];
 }
 
 // ---- optional launch timing (process-global) ----
@@ -466,7 +471,10 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
       a.cols_p = (int32_t)(P.tr ? P.np : P.mp);
       a.same = P.tr ? ptr(kX0T) : ptr(kX0);
       a.swap = P.tr ? ptr(kX0) : ptr(kX0T);
-      a.stride = P.np * P.mp;
+      a.ld_same = P.tr ? P.ld[kX0T] : P.ld[kX0];
+      a.ld_swap = P.tr ? P.ld[kX0] : P.ld[kX0T];
+      a.s_same = elem_stride(P, P.tr ? kX0T : kX0);
+      a.s_swap = elem_stride(P, P.tr ? kX0 : kX0T);
       a.cdtype = P.cdtype;
       a.gscale = reinterpret_cast<float *>(ptr(kGScale));
       a.status = status;
@@ -474,9 +482,9 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
       err = launch_scale(a, s);
     } else {
       GemmArgs a;
-      a.A = ptr(L.A); a.lda = P.cols[L.A]; a.sA = elem_stride(P, L.A);
-      a.B = ptr(L.B); a.ldb = P.cols[L.B]; a.sB = elem_stride(P, L.B);
-      if (L.Cin >= 0) { a.Cin = ptr(L.Cin); a.ldc = P.cols[L.Cin]; a.sC = elem_stride(P, L.Cin); }
+      a.A = ptr(L.A); a.lda = P.ld[L.A]; a.sA = elem_stride(P, L.A);
+      a.B = ptr(L.B); a.ldb = P.ld[L.B]; a.sB = elem_stride(P, L.B);
+      if (L.Cin >= 0) { a.Cin = ptr(L.Cin); a.ldc = P.ld[L.Cin]; a.sC = elem_stride(P, L.Cin); }
       if (L.out0 == kOutUser) {
         a.out0 = out;
         a.ld0 = C;  // the caller's [R, C] layout; final launches produce exactly that
@@ -485,11 +493,11 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
         a.out0_pad = 0;
         a.status = status;
       } else if (L.out0 >= 0) {
-        a.out0 = ptr(L.out0); a.ld0 = P.cols[L.out0]; a.s0 = elem_stride(P, L.out0);
+        a.out0 = ptr(L.out0); a.ld0 = P.ld[L.out0]; a.s0 = elem_stride(P, L.out0);
         a.out0_dtype = P.cdtype; a.out0_pad = 1;
       }
-      if (L.out1 >= 0) { a.out1 = ptr(L.out1); a.ld1 = P.cols[L.out1]; a.s1 = elem_stride(P, L.out1); }
-      if (L.out2 >= 0) { a.out2 = ptr(L.out2); a.ld2 = P.cols[L.out2]; a.s2 = elem_stride(P, L.out2); }
+      if (L.out1 >= 0) { a.out1 = ptr(L.out1); a.ld1 = P.ld[L.out1]; a.s1 = elem_stride(P, L.out1); }
+      if (L.out2 >= 0) { a.out2 = ptr(L.out2); a.ld2 = P.ld[L.out2]; a.s2 = elem_stride(P, L.out2); }
       a.diag = L.diag;
       a.M = L.M; a.N = L.N; a.K = L.K; a.Mv = L.Mv; a.Nv = L.Nv;
       a.alpha = L.alpha; a.beta = L.beta;
@@ -551,8 +559,9 @@ nsg_status_t nsg_copy(const void *src, void *dst, size_t bytes, void *stream) {
 nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_t M, int64_t N, int64_t K,
                          const void *A, int64_t lda, const void *B, int64_t ldb, float alpha, float beta,
                          const void *Cin, int64_t ldc, void *out, int64_t ldo, void *out_t, int64_t ldt,
-                         void *out_d, float diag, void *stream) {
+                         void *out_d, float diag, int32_t tile, void *stream) {
   if (!valid_dtype(dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (tile != 0 && tile != 128 && tile != 256) return NSG_ERR_INVALID_ARG;
   if (batch < 0 || M < 0 || N < 0 || K < 0) return NSG_ERR_SHAPE;
   if (batch == 0 || M == 0 || N == 0) return NSG_OK;
   if (M % kPad || N % kPad || K % kPad || K == 0 || batch > 65535 || M > NSG_MAX_SIDE || N > NSG_MAX_SIDE ||
@@ -577,7 +586,7 @@ nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_
   a.M = (int32_t)M; a.N = (int32_t)N; a.K = (int32_t)K; a.Mv = (int32_t)M; a.Nv = (int32_t)N;
   a.alpha = alpha; a.beta = beta;
   a.batch = (int32_t)batch;
-  const int cfg = choose_cfg(M, N, dtype);
+  const int cfg = tile == 0 ? choose_cfg(M, N, dtype) : (tile == 256 ? kTile256 : kTile128);
   return launch_gemm(dtype, symmetric != 0, cfg, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? NSG_OK
              : NSG_ERR_HIP;

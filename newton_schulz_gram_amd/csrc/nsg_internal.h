@@ -79,7 +79,8 @@ struct ScaleArgs {
   int32_t rows_p = 0, cols_p = 0;  // padded dims of the input's own layout
   void *same = nullptr;  // rows_p x cols_p, the input's layout
   void *swap = nullptr;  // cols_p x rows_p, transposed
-  int64_t stride = 0;    // rows_p * cols_p elements per matrix in same/swap
+  int64_t ld_same = 0, ld_swap = 0;  // row pitches (elements)
+  int64_t s_same = 0, s_swap = 0;    // elements per matrix
   int32_t cdtype = NSG_F16;
   float *gscale = nullptr;
   int32_t *status = nullptr;

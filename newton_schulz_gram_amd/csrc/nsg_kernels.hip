@@ -27,6 +27,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 template <int DT> struct Mfma;
 
@@ -68,69 +69,119 @@ template <> __device__ __forceinline__ float cvt<float>(float v) { return v; }
 
 template <typename T> struct V4 { typedef T type __attribute__((ext_vector_type(4))); };
 
-// Row-major store of a wave's accumulator tiles (values already final), with
-// the mirrored store for symmetric launches.  Outside the valid Mv x Nv corner
-// zeros are written when `pad`, nothing otherwise.  Inside a diagonal tile only
-// the lower half is stored, to both (i, j) and (j, i).  Returns whether every
-// valid stored value is finite after rounding.
-template <typename TO, bool SYM, int TM, int TN>
-__device__ __forceinline__ bool store_tile(const f32x16 (&acc)[TM][TN], TO *o, int64_t ld, int row0, int col0,
-                                           int lane, int Mv, int Nv, bool pad, bool diag_tile) {
+// fp32 epilogue of one wave's TM x TN accumulator tiles, one 32x32 tile at a
+// time (16 values per lane live at once):
+//   v = alpha' acc + beta' Cin   (0 outside the valid Mv x Nv corner)
+//   out0 = v (row-major; symmetric launches also write the mirror (j, i);
+//          inside a diagonal tile only the lower half is stored, to both
+//          places, so the result is exactly symmetric)
+//   out1 = v^T (general launches), out2 = v + diag I (symmetric launches).
+// out0 writes zeros outside the valid corner when out0_pad, nothing otherwise;
+// workspace outputs always cover the padding.  Accumulator layout of a 32x32
+// MFMA tile: lane l, register r holds row 8 (r/4) + 4 (l/32) + r%4, column
+// l%32, so 4 consecutive registers are 4 consecutive rows of one column.
+template <typename T, typename TO, bool SYM, int TM, int TN>
+__device__ __forceinline__ void epilogue(const GemmArgs &p, const f32x16 (&acc)[TM][TN], int g, bool diag_tile,
+                                         int row0, int col0, int lane) {
+  float sc = 1.f;
+  if (p.gscale != nullptr && p.gpow > 0) {
+    const float sg = p.gscale[g];
+    sc = (p.gpow == 1) ? sg : sg * sg;
+  }
+  const float alpha = p.alpha * sc, beta = p.beta * sc;
+  const T *cin = p.Cin ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
+  TO *o0 = p.out0 ? reinterpret_cast<TO *>(p.out0) + (size_t)g * p.s0 : nullptr;
+  T *o1 = p.out1 ? reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1 : nullptr;
+  T *o2 = p.out2 ? reinterpret_cast<T *>(p.out2) + (size_t)g * p.s2 : nullptr;
+  const bool pad0 = p.out0_pad != 0;
   bool finite = true;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = col0 + j * 32 + (lane & 31);
+      f32x16 v;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        float x = alpha * acc[i][j][r];
+        if (cin != nullptr) x += beta * (float)cin[(size_t)row * p.ldc + col];
+        v[r] = (row < p.Mv && col < p.Nv) ? x : 0.f;
+      }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int rowb = row0 + i * 32 + 8 * r4 + 4 * (lane >> 5);
-        typename V4<TO>::type h;
+        if (o0 != nullptr) {
+          typename V4<TO>::type h;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = cvt<TO>(acc[i][j][r4 * 4 + q]);
+          for (int q = 0; q < 4; ++q) h[q] = cvt<TO>(v[r4 * 4 + q]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = rowb + q;
-          const bool valid = row < Mv && col < Nv;
-          if ((valid || pad) && (!diag_tile || row >= col)) {
-            o[(size_t)row * ld + col] = h[q];
-            finite = finite && (!valid || __builtin_isfinite((float)h[q]));
+          for (int q = 0; q < 4; ++q) {
+            const int row = rowb + q;
+            const bool valid = row < p.Mv && col < p.Nv;
+            if ((valid || pad0) && (!diag_tile || row >= col)) {
+              o0[(size_t)row * p.ld0 + col] = h[q];
+              finite = finite && (!valid || __builtin_isfinite((float)h[q]));
+            }
+          }
+          if constexpr (SYM) {
+            if (!diag_tile) {
+              *reinterpret_cast<typename V4<TO>::type *>(o0 + (size_t)col * p.ld0 + rowb) = h;
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (rowb + q > col) o0[(size_t)col * p.ld0 + rowb + q] = h[q];
+            }
+          }
+        }
+        if constexpr (!SYM) {
+          if (o1 != nullptr) {
+            typename V4<T>::type h;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = cvt<T>(v[r4 * 4 + q]);
+            *reinterpret_cast<typename V4<T>::type *>(o1 + (size_t)col * p.ld1 + rowb) = h;
           }
         }
         if constexpr (SYM) {
-          if (!diag_tile) {
-            *reinterpret_cast<typename V4<TO>::type *>(o + (size_t)col * ld + rowb) = h;
-          } else {
+          if (o2 != nullptr) {
+            typename V4<T>::type h;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = rowb + q;
+              h[q] = cvt<T>((row == col && row < p.Mv) ? v[r4 * 4 + q] + p.diag : v[r4 * 4 + q]);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              if (rowb + q > col) o[(size_t)col * ld + rowb + q] = h[q];
+              if (!diag_tile || rowb + q >= col) o2[(size_t)(rowb + q) * p.ld2 + col] = h[q];
+            if (!diag_tile) {
+              *reinterpret_cast<typename V4<T>::type *>(o2 + (size_t)col * p.ld2 + rowb) = h;
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (rowb + q > col) o2[(size_t)col * p.ld2 + rowb + q] = h[q];
+            }
           }
         }
       }
     }
   }
-  return finite;
+  if (p.status != nullptr && __ballot(!finite) != 0 && lane == 0) p.status[g] = 1;
 }
 
-// Transposed store (V^T), 4 consecutive rows of V per lane = 4 contiguous
-// elements of V^T.  Workspace output: every element, zeros already in place.
-template <typename TO, int TM, int TN>
-__device__ __forceinline__ void store_tile_t(const f32x16 (&acc)[TM][TN], TO *o, int64_t ld, int row0, int col0,
-                                             int lane) {
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = col0 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int rowb = row0 + i * 32 + 8 * r4 + 4 * (lane >> 5);
-        typename V4<TO>::type h;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = cvt<TO>(acc[i][j][r4 * 4 + q]);
-        *reinterpret_cast<typename V4<TO>::type *>(o + (size_t)col * ld + rowb) = h;
-      }
-    }
+template <typename T, bool SYM, int TM, int TN>
+__device__ __forceinline__ void run_epilogue(const GemmArgs &p, const f32x16 (&acc)[TM][TN], int g, bool diag_tile,
+                                             int row0, int col0, int lane) {
+  if constexpr (SYM) {
+    // symmetric products only ever write workspace buffers (compute dtype)
+    epilogue<T, T, SYM, TM, TN>(p, acc, g, diag_tile, row0, col0, lane);
+    return;
+  }
+  if (p.out0_dtype == NSG_F16)
+    epilogue<T, _Float16, SYM, TM, TN>(p, acc, g, diag_tile, row0, col0, lane);
+  else if (p.out0_dtype == NSG_BF16)
+    epilogue<T, __bf16, SYM, TM, TN>(p, acc, g, diag_tile, row0, col0, lane);
+  else
+    epilogue<T, float, SYM, TM, TN>(p, acc, g, diag_tile, row0, col0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -248,70 +299,182 @@ gemm_nt_kernel(const GemmArgs p) {
   }
 
   // ---- fp32 epilogue ----
-  // Accumulator layout of a 32x32 MFMA tile: lane l, register r holds
-  // row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-  float sc = 1.f;
-  if (p.gscale != nullptr && p.gpow > 0) {
-    const float s = p.gscale[g];
-    sc = (p.gpow == 1) ? s : s * s;
-  }
-  const float alpha = p.alpha * sc, beta = p.beta * sc;
-  const int row0 = tm * BM + wm * WM, col0 = tn * BN + wn * WN;
-  const T *cin = p.Cin ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = col0 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        float v = alpha * acc[i][j][r];
-        if (cin != nullptr) v += beta * (float)cin[(size_t)row * p.ldc + col];
-        acc[i][j][r] = (row < p.Mv && col < p.Nv) ? v : 0.f;
-      }
-    }
-  }
-  const bool diag_tile = SYM && (tm == tn);
-  if (p.out0 != nullptr) {
-    bool fin = true;
-    if (p.out0_dtype == NSG_F16)
-      fin = store_tile<_Float16, SYM, TM, TN>(acc, reinterpret_cast<_Float16 *>(p.out0) + (size_t)g * p.s0, p.ld0,
-                                              row0, col0, lane, p.Mv, p.Nv, p.out0_pad != 0, diag_tile);
-    else if (p.out0_dtype == NSG_BF16)
-      fin = store_tile<__bf16, SYM, TM, TN>(acc, reinterpret_cast<__bf16 *>(p.out0) + (size_t)g * p.s0, p.ld0,
-                                            row0, col0, lane, p.Mv, p.Nv, p.out0_pad != 0, diag_tile);
-    else
-      fin = store_tile<float, SYM, TM, TN>(acc, reinterpret_cast<float *>(p.out0) + (size_t)g * p.s0, p.ld0,
-                                           row0, col0, lane, p.Mv, p.Nv, p.out0_pad != 0, diag_tile);
-    if (p.status != nullptr && __ballot(!fin) != 0 && lane == 0) p.status[g] = 1;
-  }
-  if constexpr (!SYM) {
-    if (p.out1 != nullptr)
-      store_tile_t<T, TM, TN>(acc, reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1, p.ld1, row0, col0, lane);
-  }
-  if constexpr (SYM) {
-    if (p.out2 != nullptr) {
-      // second store of the same accumulator with + diag on the (valid) diagonal
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = col0 + j * 32 + (lane & 31);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row == col && row < p.Mv) acc[i][j][r] += p.diag;
-          }
-        }
-      store_tile<T, true, TM, TN>(acc, reinterpret_cast<T *>(p.out2) + (size_t)g * p.s2, p.ld2, row0, col0, lane,
-                                  p.Mv, p.Nv, true, diag_tile);
-    }
-  }
+  run_epilogue<T, SYM, TM, TN>(p, acc, g, SYM && (tm == tn), tm * BM + wm * WM, tn * BN + wn * WN, lane);
 }
 
 #undef NSG_GLOAD
 #undef NSG_SWRITE
+
+// ---------------------------------------------------------------------------
+// 256x256 batched NT GEMM for large matrices.  NW waves (2 along M), each
+// owning a 128 x (512/NW) block of 32x32 MFMA tiles.  Operands stream
+// global -> LDS with direct loads (global_load_lds_dwordx4, no register
+// staging) through a ring of NSTAGE stages of 64-byte row slices (32 fp16 /
+// bf16 or 16 fp32 K elements), so the loads of NSTAGE-1 stages are in flight
+// while one stage feeds the MFMAs: enough to cover L2-miss latency.
+//
+// LDS layout of one 256-row operand slice: row-major, 64 bytes (4 16-byte
+// chunks) per row, with chunk c of row r stored at chunk slot c ^ f(r),
+// f(r) = ((r >> 1) ^ (r >> 3)) & 3.  A direct-load instruction fills 1 KB =
+// 16 rows, each group of 4 consecutive lanes reading one row's 64 contiguous
+// bytes (so the address coalescer sees whole segments); the swizzle spreads
+// an MFMA fragment read of 16 consecutive rows at one chunk over distinct
+// banks.
+//
+// Tile order: the dispatcher hands consecutive workgroups to the 8 XCDs in
+// turn, so the linear block id is remapped to give each XCD a contiguous run
+// of (matrix, tile) work; within a matrix, tiles go in groups of 4 tile rows
+// (column by column) so concurrent workgroups of one XCD share operand rows
+// in its L2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int slice_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int lds_slice_off(int r, int c) { return r * 64 + ((c ^ slice_swz(r)) << 4); }
+
+// One direct global -> LDS load of 16 bytes per lane: lane l reads
+// base + voff (bytes) and writes LDS bytes [lds + 16 l, lds + 16 l + 16).
+// Issued as inline assembly so that the compiler does not add waits for it
+// before unrelated LDS reads; the kernel waits (vmcnt) and synchronizes itself
+// before reading a stage.
+__device__ __forceinline__ void lds_dma16(const void *base, unsigned voff, const void *lds) {
+  const unsigned m0v = (unsigned)(size_t)(lds_ptr_t)lds;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0v) : "memory");
+}
+
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+constexpr int kStages256 = 4;
+
+template <int DT, bool SYM, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
+  using MF = Mfma<DT>;
+  using T = typename MF::T;
+  using frag_t = typename MF::frag_t;
+  constexpr int ES = (int)sizeof(T);
+  constexpr int BK = 64 / ES;        // K elements per stage (64-byte row slices)
+  constexpr int CE = 16 / ES;        // elements per 16-byte chunk
+  constexpr int SLICE = 256 * 64;    // bytes of one operand slice
+  constexpr int STAGE = 2 * SLICE;   // A slice then B slice
+  constexpr int NST = kStages256;
+  constexpr int S = BK / MF::KPER;   // MFMA K-steps per stage
+  constexpr int WGN = NW / 2;        // waves along N (2 along M)
+  constexpr int WN = 256 / WGN;      // wave tile: 128 x WN
+  constexpr int TN = WN / 32;
+  constexpr int NLD = 16 / NW;       // 1 KB direct loads per operand per wave per stage
+  static_assert(NLD >= 1 && 16 % NW == 0, "waves");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NST * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // ---- block id -> (matrix, tile) ----
+  const unsigned L = blockIdx.x, total = gridDim.x;
+  const unsigned xcd = L & 7u, slot = L >> 3, per = total >> 3, rem = total & 7u;
+  const unsigned V = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int tiles_m = p.M >> 8, tiles_n = p.N >> 8;
+  const int tiles = SYM ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
+  const int g = (int)(V / (unsigned)tiles);
+  const int t = (int)(V - (unsigned)g * (unsigned)tiles);
+  int tm, tn;
+  if constexpr (SYM) {
+    int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+    while (r * (r + 1) / 2 > t) --r;
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    tm = r;
+    tn = t - r * (r + 1) / 2;
+  } else {
+    constexpr int GM = 4;
+    const int in_group = GM * tiles_n;
+    const int first = (t / in_group) * GM;
+    const int gsz = min(tiles_m - first, GM);
+    const int w = t - (t / in_group) * in_group;
+    tm = first + w % gsz;
+    tn = w / gsz;
+  }
+
+  // ---- direct-load sources: wave w fills the 1 KB blocks b = w + NW i of
+  //      each slice (rows 16 b .. 16 b + 15; lane l writes chunk slot l % 4
+  //      of row 16 b + l / 4, i.e. logical chunk (l % 4) ^ f(row)) ----
+  const T *gA = reinterpret_cast<const T *>(p.A) + (size_t)g * p.sA + (size_t)tm * 256 * p.lda;
+  const T *gB = reinterpret_cast<const T *>(p.B) + (size_t)g * p.sB + (size_t)tn * 256 * p.ldb;
+  unsigned offA[NLD], offB[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int b = wave + NW * i;
+    const int row = b * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ slice_swz(row);
+    offA[i] = (unsigned)((row * (int)p.lda + chunk * CE) * ES);
+    offB[i] = (unsigned)((row * (int)p.ldb + chunk * CE) * ES);
+  }
+  auto issue = [&](int kt) {
+    unsigned char *st = lds + (kt % NST) * STAGE;
+    const T *a = gA + (size_t)kt * BK;
+    const T *b = gB + (size_t)kt * BK;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      lds_dma16(a, offA[i], st + (wave + NW * i) * 1024);
+      lds_dma16(b, offB[i], st + SLICE + (wave + NW * i) * 1024);
+    }
+  };
+
+  // ---- fragment reads: lane l reads row (block row + l%32) at K element
+  //      ks + (l/32) FE of the stage ----
+  const int rA = wm * 128 + (lane & 31), rB = wn * WN + (lane & 31);
+  const int h = lane >> 5;
+  auto frag_off = [&](int rbase, int i, int s) -> int {
+    const int k = s * MF::KPER + h * MF::FE;
+    return lds_slice_off(rbase + i * 32, k / CE) + (k % CE) * ES;
+  };
+  f32x16 acc[4][TN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = p.K / BK;  // >= 8: K is a multiple of 256
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt have landed once at most the loads of
+    // the stages issued after it are outstanding
+    if (kt + NST - 2 < nk) wait_vmcnt<2 * NLD * (NST - 2)>();
+    else if (kt + 1 < nk) wait_vmcnt<2 * NLD>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's loads of stage kt landed; stage kt-1 is free
+    if (kt + NST - 1 < nk) issue(kt + NST - 1);
+    const unsigned char *st = lds + (kt % NST) * STAGE;
+    frag_t fa[2][4], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const frag_t *>(st + frag_off(rA, i, 0));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = *reinterpret_cast<const frag_t *>(st + SLICE + frag_off(rB, j, 0));
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (s + 1 < S) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fa[(s + 1) & 1][i] = *reinterpret_cast<const frag_t *>(st + frag_off(rA, i, s + 1));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          fb[(s + 1) & 1][j] = *reinterpret_cast<const frag_t *>(st + SLICE + frag_off(rB, j, s + 1));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+    }
+  }
+
+  // ---- fp32 epilogue (same contract as gemm_nt_kernel) ----
+  run_epilogue<T, SYM, 4, TN>(p, acc, g, SYM && (tm == tn), tm * 256 + wm * 128, tn * 256 + wn * WN, lane);
+}
 
 int tile_m(int cfg) { return cfg == kTile256 ? 256 : 128; }
 
@@ -344,9 +507,21 @@ static hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+constexpr int kWaves256 = 8;
+
+template <int DT, bool SYM>
+static hipError_t launch_256(const GemmArgs &a, hipStream_t s) {
+  const unsigned tm = (unsigned)(a.M / 256), tn = (unsigned)(a.N / 256);
+  const unsigned tiles = SYM ? tm * (tm + 1) / 2 : tm * tn;
+  const unsigned long long blocks = (unsigned long long)tiles * (unsigned)a.batch;
+  if (blocks == 0 || blocks > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm256_kernel<DT, SYM, kWaves256>), dim3((unsigned)blocks), dim3(kWaves256 * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int DT, bool SYM>
 static hipError_t launch_cfg(int cfg, const GemmArgs &a, hipStream_t s) {
-  if (cfg == kTile256) return launch_one<DT, 256, 256, 2, 2, SYM>(a, s);
+  if (cfg == kTile256) return launch_256<DT, SYM>(a, s);
   return launch_one<DT, 128, 128, 2, 2, SYM>(a, s);
 }
 
@@ -437,14 +612,14 @@ __global__ void __launch_bounds__(256) scale_cast_transpose_kernel(const ScaleAr
     tile[a][b] = ldexpf(v, e);
   }
   __syncthreads();
-  TO *same = reinterpret_cast<TO *>(p.same) + (size_t)g * p.stride;
-  TO *swp = reinterpret_cast<TO *>(p.swap) + (size_t)g * p.stride;
+  TO *same = reinterpret_cast<TO *>(p.same) + (size_t)g * p.s_same;
+  TO *swp = reinterpret_cast<TO *>(p.swap) + (size_t)g * p.s_swap;
 #pragma unroll 4
   for (int it = 0; it < 16; ++it) {
     const int idx = it * 256 + tid;
     const int a = idx >> 6, b = idx & 63;
-    same[(size_t)(a0 + a) * p.cols_p + (b0 + b)] = cvt<TO>(tile[a][b]);
-    swp[(size_t)(b0 + a) * p.rows_p + (a0 + b)] = cvt<TO>(tile[b][a]);
+    same[(size_t)(a0 + a) * p.ld_same + (b0 + b)] = cvt<TO>(tile[a][b]);
+    swp[(size_t)(b0 + a) * p.ld_swap + (a0 + b)] = cvt<TO>(tile[b][a]);
   }
 }
 

@@ -23,42 +23,45 @@ def rel(x, y):
     return float((x.float() - y.float()).norm() / y.float().norm().clamp_min(1e-30))
 
 
+@pytest.mark.parametrize("tile", [128, 256])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("MNK", [(256, 256, 256), (512, 768, 256), (256, 512, 1024)])
-def test_general_gemm(dtype, MNK):
+@pytest.mark.parametrize("MNK", [(256, 256, 256), (512, 768, 256), (256, 512, 1024), (1024, 768, 512)])
+def test_general_gemm(dtype, MNK, tile):
     M, N, K = MNK
     g = torch.Generator(device="cuda").manual_seed(1)
     A = torch.randn(3, M, K, device="cuda", generator=g).to(dtype)
     B = torch.randn(3, N, K, device="cuda", generator=g).to(dtype)
     Cin = torch.randn(3, M, N, device="cuda", generator=g).to(dtype)
-    out, out_t, _ = nsg.gemm_nt(A, B, alpha=0.5, beta=-1.25, Cin=Cin, transposed_out=True)
+    out, out_t, _ = nsg.gemm_nt(A, B, alpha=0.5, beta=-1.25, Cin=Cin, transposed_out=True, tile=tile)
     torch.cuda.synchronize()
     ref = ref_nt(A, B, 0.5, -1.25, Cin)
     assert rel(out, ref) <= TOL[dtype]
     assert torch.equal(out_t, out.transpose(1, 2).contiguous())
 
 
+@pytest.mark.parametrize("tile", [128, 256])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("n,K", [(256, 512), (768, 256), (1024, 1024)])
-def test_symmetric_gemm_gram(dtype, n, K):
+def test_symmetric_gemm_gram(dtype, n, K, tile):
     """X X^T on the lower-triangle tiles only, mirrored: exactly symmetric."""
     g = torch.Generator(device="cuda").manual_seed(2)
     X = torch.randn(2, n, K, device="cuda", generator=g).to(dtype)
-    out, _, _ = nsg.gemm_nt(X, X, alpha=2.0, symmetric=True)
+    out, _, _ = nsg.gemm_nt(X, X, alpha=2.0, symmetric=True, tile=tile)
     torch.cuda.synchronize()
     assert torch.equal(out, out.transpose(1, 2))
     assert rel(out, ref_nt(X, X, 2.0)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("tile", [128, 256])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
-def test_symmetric_quadratic_with_dual_store(dtype):
+def test_symmetric_quadratic_with_dual_store(dtype, tile):
     """Z = b R + c R R^T (R symmetric) and the second store Z + a I."""
     g = torch.Generator(device="cuda").manual_seed(3)
     n = 512
     X = torch.randn(1, n, 1024, device="cuda", generator=g) / 32
     R = (X @ X.transpose(1, 2)).to(dtype)
     R = ((R.float() + R.float().transpose(1, 2)) / 2).to(dtype)  # exactly symmetric
-    Z, _, Q = nsg.gemm_nt(R, R, alpha=2.0315, beta=-4.775, Cin=R, symmetric=True, diag=3.4445)
+    Z, _, Q = nsg.gemm_nt(R, R, alpha=2.0315, beta=-4.775, Cin=R, symmetric=True, diag=3.4445, tile=tile)
     torch.cuda.synchronize()
     ref = ref_nt(R, R, 2.0315, -4.775, R)
     assert torch.equal(Z, Z.transpose(1, 2)) and torch.equal(Q, Q.transpose(1, 2))
@@ -73,3 +76,20 @@ def test_gemm_rejects_unpadded_sizes():
     A = torch.zeros(1, 200, 256, device="cuda", dtype=torch.float16)
     with pytest.raises(nsg.NSGError):
         nsg.gemm_nt(A, A)
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+def test_symmetric_product_of_distinct_operands_is_mirrored(tile):
+    """Z (RZ) with RZ not exactly symmetric: only the lower triangle is computed
+    and mirrored, so the output is exactly symmetric and equals the lower
+    triangle of the full product."""
+    g = torch.Generator(device="cuda").manual_seed(4)
+    n = 768
+    Z = torch.randn(2, n, n, device="cuda", generator=g).half()
+    W = torch.randn(2, n, n, device="cuda", generator=g).half()
+    out, _, _ = nsg.gemm_nt(Z, W, symmetric=True, tile=tile)
+    torch.cuda.synchronize()
+    ref = ref_nt(Z, W)
+    low = torch.tril(torch.ones(n, n, device="cuda", dtype=torch.bool))
+    assert torch.equal(out, out.transpose(1, 2))
+    assert rel(out[:, low], ref[:, low]) <= TOL[torch.float16]
