@@ -252,13 +252,17 @@ def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 
     Returns (V, V^T or None, V + diag I or None)."""
     b, M, K = A.shape
     N = B.shape[1]
+    for t in (A, B) + ((Cin,) if Cin is not None else ()):
+        if t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError("gemm_nt operands need unit column stride and packed batches")
     out = torch.empty((b, M, N), dtype=A.dtype, device=A.device)
     out_t = torch.empty((b, N, M), dtype=A.dtype, device=A.device) if transposed_out else None
     out_d = torch.empty((b, M, N), dtype=A.dtype, device=A.device) if diag is not None else None
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
     with torch.cuda.device(A.device):
         code = lib().nsg_gemm_nt(_dtype_code(A.dtype), 1 if symmetric else 0, b, M, N, K,
-                                 ptr(A), K, ptr(B), K, float(alpha), float(beta), ptr(Cin), N,
+                                 ptr(A), A.stride(1), ptr(B), B.stride(1), float(alpha), float(beta), ptr(Cin),
+                                 Cin.stride(1) if Cin is not None else N,
                                  ptr(out), N, ptr(out_t), M, ptr(out_d), float(diag or 0.0), int(tile),
                                  ctypes.c_void_p(_stream_handle(A.device)))
     _check(code, "nsg_gemm_nt")

@@ -307,28 +307,27 @@ gemm_nt_kernel(const GemmArgs p) {
 
 // ---------------------------------------------------------------------------
 // 256x256 batched NT GEMM for large matrices.  NW waves (2 along M), each
-// owning a 128 x (512/NW) block of 32x32 MFMA tiles.  Operands stream
-// global -> LDS with direct loads (global_load_lds_dwordx4, no register
-// staging) through a ring of NSTAGE stages of 64-byte row slices (32 fp16 /
-// bf16 or 16 fp32 K elements), so the loads of NSTAGE-1 stages are in flight
-// while one stage feeds the MFMAs: enough to cover L2-miss latency.
+// owning a 128 x (512/NW) block of 32x32 MFMA tiles (NW = 4: 128x128, 256
+// fp32 accumulators per lane).  Operands stream global -> LDS with direct
+// loads (global_load_lds_dwordx4, no register staging) in stages of 128-byte
+// row slices (64 fp16 / bf16 or 32 fp32 K elements), double buffered; the
+// loads of stage k+1 are in flight while stage k feeds the MFMAs.  Whole
+// 128-byte lines matter: measured L2 -> LDS throughput with half-line (64 B)
+// row segments is half that with full lines.
 //
-// LDS layout of one 256-row operand slice: row-major, 64 bytes (4 16-byte
-// chunks) per row, with chunk c of row r stored at chunk slot c ^ f(r),
-// f(r) = ((r >> 1) ^ (r >> 3)) & 3.  A direct-load instruction fills 1 KB =
-// 16 rows, each group of 4 consecutive lanes reading one row's 64 contiguous
-// bytes (so the address coalescer sees whole segments); the swizzle spreads
-// an MFMA fragment read of 16 consecutive rows at one chunk over distinct
-// banks.
+// LDS layout of one 256-row operand slice: row-major, 128 bytes (8 16-byte
+// chunks) per row, chunk c of row r stored at chunk slot c ^ f(r),
+// f(r) = (r ^ (r >> 3)) & 7.  A direct-load instruction fills 1 KB = 8 rows,
+// each group of 8 consecutive lanes reading one row's 128 contiguous bytes;
+// the swizzle spreads an MFMA fragment read of 16 (or 8) consecutive rows at
+// one chunk over distinct banks.
 //
-// Tile order: the dispatcher hands consecutive workgroups to the 8 XCDs in
-// turn, so the linear block id is remapped to give each XCD a contiguous run
-// of (matrix, tile) work; within a matrix, tiles go in groups of 4 tile rows
-// (column by column) so concurrent workgroups of one XCD share operand rows
-// in its L2.
+// Tile order: within a matrix, tiles go in groups of 4 tile rows (column by
+// column); the block id -> tile map below gives each XCD 32 consecutive tiles
+// of that order at a time, all XCDs working on the same matrix.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int slice_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-__device__ __forceinline__ int lds_slice_off(int r, int c) { return r * 64 + ((c ^ slice_swz(r)) << 4); }
+__device__ __forceinline__ int slice_swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int lds_slice_off(int r, int c) { return r * 128 + ((c ^ slice_swz(r)) << 4); }
 
 // One direct global -> LDS load of 16 bytes per lane: lane l reads
 // base + voff (bytes) and writes LDS bytes [lds + 16 l, lds + 16 l + 16).
@@ -346,7 +345,195 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-constexpr int kStages256 = 4;
+constexpr int kStages256 = 2;
+
+// 16-byte vector of 8 16-bit values, or of 4 floats.
+template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_type(16 / sizeof(TO)))); };
+
+// Epilogue of a 256x256 tile through LDS, in two passes of 128 rows.
+//   A: the waves owning the pass's rows write their fp32 accumulators into
+//      LDS, column-major (column c of the tile at c * PITCH floats), one
+//      16-byte write per 4 consecutive rows.
+//   B1: every thread takes 8 rows x 8 columns per step (a wave covers 8 rows
+//      x 64 columns: whole 128-byte lines of the row-major operands), forms
+//      v = alpha' acc + beta' Cin (0 outside the valid corner), writes v back
+//      to LDS and stores out0 (and out2 = v + diag I) row-major.
+//   B2: every thread takes 8 consecutive rows of one column (4 columns per
+//      wave step = 4 whole output rows of 256 bytes) and stores the transposed
+//      copy: the mirror (j, i) of a symmetric product, or out1 = V^T.
+// Inside a diagonal tile of a symmetric product only the lower half is
+// stored, to both places, so the output is exactly symmetric.
+template <typename T, typename TO, bool SYM, int NW, int TN, int PITCH>
+__device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x16 (&acc)[4][TN], float *lds, int g,
+                                                  int tm, int tn, int wm, int wn, int lane, int tid) {
+  constexpr int NT = NW * 64;
+  constexpr int WN = TN * 32;
+  constexpr int VT = 16 / (int)sizeof(T);   // elements of T per 16 bytes
+  constexpr int VO = 16 / (int)sizeof(TO);  // elements of TO per 16 bytes
+  float sc = 1.f;
+  if (p.gscale != nullptr && p.gpow > 0) {
+    const float sg = p.gscale[g];
+    sc = (p.gpow == 1) ? sg : sg * sg;
+  }
+  const float alpha = p.alpha * sc, beta = p.beta * sc;
+  const T *cin = p.Cin ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
+  TO *o0 = p.out0 ? reinterpret_cast<TO *>(p.out0) + (size_t)g * p.s0 : nullptr;
+  T *o1 = p.out1 ? reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1 : nullptr;
+  T *o2 = p.out2 ? reinterpret_cast<T *>(p.out2) + (size_t)g * p.s2 : nullptr;
+  const bool pad0 = p.out0_pad != 0;
+  const bool diag_tile = SYM && (tm == tn);
+  // 16-byte row stores need the row pitch and base of out0 to allow them
+  const bool vec0 = o0 != nullptr && (p.ld0 % VO) == 0 && ((reinterpret_cast<uintptr_t>(o0) & 15) == 0);
+  const int wave = tid >> 6;
+  bool finite = true;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int grow0 = tm * 256 + pass * 128;  // global row of staged row 0
+    const int gcol0 = tn * 256;
+    // ---- A: accumulators -> LDS ----
+    if (wm == pass) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int c = wn * WN + j * 32 + (lane & 31);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int r = i * 32 + 8 * r4 + 4 * (lane >> 5);
+            float4 v4 = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                                    acc[i][j][4 * r4 + 3]);
+            *reinterpret_cast<float4 *>(lds + c * PITCH + r) = v4;
+          }
+        }
+    }
+    __syncthreads();
+    // ---- B1: row orientation ----
+    {
+      const int rs = lane & 7, cgl = lane >> 3;  // 8 rows x 8 column groups per wave step
+#pragma unroll 1
+      for (int it = wave; it < 16 * 4; it += NW) {
+        const int rb = (it >> 2) * 8, cb = (it & 3) * 64;
+        const int r = rb + rs, c = cb + cgl * 8;
+        const int row = grow0 + r, col = gcol0 + c;
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = alpha * lds[(c + q) * PITCH + r];
+        if (cin != nullptr) {
+          typename Vec16<T>::type cv[8 / VT > 0 ? 8 / VT : 1];
+          const T *src = cin + (size_t)row * p.ldc + col;
+#pragma unroll
+          for (int u = 0; u < 8 / VT; ++u) cv[u] = *reinterpret_cast<const typename Vec16<T>::type *>(src + u * VT);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] += beta * (float)cv[q / VT][q % VT];
+        }
+        const bool rv = row < p.Mv;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (!(rv && col + q < p.Nv)) v[q] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) lds[(c + q) * PITCH + r] = v[q];
+        const bool all_valid = rv && col + 8 <= p.Nv;
+        if (o0 != nullptr) {
+          TO h[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) h[q] = cvt<TO>(v[q]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (rv && col + q < p.Nv) finite = finite && __builtin_isfinite((float)h[q]);
+          TO *dst = o0 + (size_t)row * p.ld0 + col;
+          if (vec0 && !diag_tile && (all_valid || pad0)) {
+#pragma unroll
+            for (int u = 0; u < 8 / VO; ++u) {
+              typename Vec16<TO>::type w;
+#pragma unroll
+              for (int q = 0; q < VO; ++q) w[q] = h[u * VO + q];
+              *reinterpret_cast<typename Vec16<TO>::type *>(dst + u * VO) = w;
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if ((pad0 || (rv && col + q < p.Nv)) && (!diag_tile || row >= col + q)) dst[q] = h[q];
+          }
+        }
+        if constexpr (SYM) {
+          if (o2 != nullptr) {
+            T h[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) h[q] = cvt<T>((row == col + q && rv) ? v[q] + p.diag : v[q]);
+            T *dst = o2 + (size_t)row * p.ld2 + col;
+            if (!diag_tile) {
+#pragma unroll
+              for (int u = 0; u < 8 / VT; ++u) {
+                typename Vec16<T>::type w;
+#pragma unroll
+                for (int q = 0; q < VT; ++q) w[q] = h[u * VT + q];
+                *reinterpret_cast<typename Vec16<T>::type *>(dst + u * VT) = w;
+              }
+            } else {
+#pragma unroll
+              for (int q = 0; q < 8; ++q)
+                if (row >= col + q) dst[q] = h[q];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- B2: column orientation (transposed copy) ----
+    T *ot = SYM ? reinterpret_cast<T *>(o0) : o1;  // symmetric outputs are in the compute dtype
+    const int ldt = SYM ? (int)p.ld0 : (int)p.ld1;
+#pragma unroll 1
+    for (int k = 0; k < 2; ++k) {
+      T *dstbase = (k == 0) ? ot : (SYM ? o2 : nullptr);
+      const int ldk = (k == 0) ? ldt : (int)p.ld2;
+      if (dstbase == nullptr) continue;
+      const int rg = lane & 15, cl = lane >> 4;  // 16 groups of 8 rows x 4 columns per wave step
+#pragma unroll 1
+      for (int it = wave; it < 64; it += NW) {
+        const int c = it * 4 + cl, r = rg * 8;
+        const int row = grow0 + r, col = gcol0 + c;
+        const float4 a4 = *reinterpret_cast<const float4 *>(lds + c * PITCH + r);
+        const float4 b4 = *reinterpret_cast<const float4 *>(lds + c * PITCH + r + 4);
+        const float v[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+        T h[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) h[q] = cvt<T>(v[q]);
+        T *dst = dstbase + (size_t)col * ldk + row;
+        if (!diag_tile) {
+#pragma unroll
+          for (int u = 0; u < 8 / VT; ++u) {
+            typename Vec16<T>::type w;
+#pragma unroll
+            for (int q = 0; q < VT; ++q) w[q] = h[u * VT + q];
+            *reinterpret_cast<typename Vec16<T>::type *>(dst + u * VT) = w;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (row + q > col) dst[q] = h[q];
+        }
+      }
+    }
+    __syncthreads();  // LDS is rewritten by the next pass
+  }
+  if (p.status != nullptr && __ballot(!finite) != 0 && lane == 0) p.status[g] = 1;
+}
+
+template <typename T, bool SYM, int NW, int TN, int PITCH>
+__device__ __forceinline__ void staged_epilogue(const GemmArgs &p, const f32x16 (&acc)[4][TN], float *lds, int g,
+                                                int tm, int tn, int wm, int wn, int lane, int tid) {
+  if constexpr (SYM) {
+    staged_epilogue_t<T, T, true, NW, TN, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+  } else {
+    if (p.out0_dtype == NSG_F16)
+      staged_epilogue_t<T, _Float16, false, NW, TN, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+    else if (p.out0_dtype == NSG_BF16)
+      staged_epilogue_t<T, __bf16, false, NW, TN, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+    else
+      staged_epilogue_t<T, float, false, NW, TN, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+  }
+}
+
 
 template <int DT, bool SYM, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
@@ -354,18 +541,21 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
   using T = typename MF::T;
   using frag_t = typename MF::frag_t;
   constexpr int ES = (int)sizeof(T);
-  constexpr int BK = 64 / ES;        // K elements per stage (64-byte row slices)
+  constexpr int BK = 128 / ES;       // K elements per stage (128-byte row slices)
   constexpr int CE = 16 / ES;        // elements per 16-byte chunk
-  constexpr int SLICE = 256 * 64;    // bytes of one operand slice
+  constexpr int SLICE = 256 * 128;   // bytes of one operand slice
   constexpr int STAGE = 2 * SLICE;   // A slice then B slice
   constexpr int NST = kStages256;
   constexpr int S = BK / MF::KPER;   // MFMA K-steps per stage
   constexpr int WGN = NW / 2;        // waves along N (2 along M)
   constexpr int WN = 256 / WGN;      // wave tile: 128 x WN
   constexpr int TN = WN / 32;
-  constexpr int NLD = 16 / NW;       // 1 KB direct loads per operand per wave per stage
-  static_assert(NLD >= 1 && 16 % NW == 0, "waves");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[NST * STAGE];
+  constexpr int NLD = 32 / NW;       // 1 KB direct loads per operand per wave per stage
+  static_assert(NLD >= 1 && 32 % NW == 0, "waves");
+  constexpr int EPI_PITCH = 132;  // floats per staged column (128 rows + 4)
+  constexpr int EPI_BYTES = 256 * EPI_PITCH * 4;
+  constexpr int LDS_BYTES = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -373,9 +563,20 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
   const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- block id -> (matrix, tile) ----
+  // Workgroups reach the XCDs round-robin (block L on XCD L % 8).  Rounds of
+  // 8 x 32 consecutive tiles are split so XCD x takes chunk x (32 tiles = the
+  // workgroups it runs at once, a 4 x 8 block of the grouped order below): the
+  // 8 XCDs then work on neighbouring tiles of the same matrix, whose operands
+  // stay in the shared last-level cache, while each XCD's 32 tiles share rows
+  // in its own L2.  The tail that does not fill a round keeps the identity map.
   const unsigned L = blockIdx.x, total = gridDim.x;
-  const unsigned xcd = L & 7u, slot = L >> 3, per = total >> 3, rem = total & 7u;
-  const unsigned V = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  constexpr unsigned CH = 32, ROUND = 8 * CH;
+  const unsigned full = total / ROUND;
+  unsigned V = L;
+  if (L < full * ROUND) {
+    const unsigned xcd = L & 7u, slot = L >> 3;
+    V = (slot / CH) * ROUND + xcd * CH + (slot % CH);
+  }
   const int tiles_m = p.M >> 8, tiles_n = p.N >> 8;
   const int tiles = SYM ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
   const int g = (int)(V / (unsigned)tiles);
@@ -398,16 +599,16 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
   }
 
   // ---- direct-load sources: wave w fills the 1 KB blocks b = w + NW i of
-  //      each slice (rows 16 b .. 16 b + 15; lane l writes chunk slot l % 4
-  //      of row 16 b + l / 4, i.e. logical chunk (l % 4) ^ f(row)) ----
+  //      each slice (rows 8 b .. 8 b + 7; lane l writes chunk slot l % 8 of
+  //      row 8 b + l / 8, i.e. logical chunk (l % 8) ^ f(row)) ----
   const T *gA = reinterpret_cast<const T *>(p.A) + (size_t)g * p.sA + (size_t)tm * 256 * p.lda;
   const T *gB = reinterpret_cast<const T *>(p.B) + (size_t)g * p.sB + (size_t)tn * 256 * p.ldb;
   unsigned offA[NLD], offB[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int b = wave + NW * i;
-    const int row = b * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ slice_swz(row);
+    const int row = b * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ slice_swz(row);
     offA[i] = (unsigned)((row * (int)p.lda + chunk * CE) * ES);
     offB[i] = (unsigned)((row * (int)p.ldb + chunk * CE) * ES);
   }
@@ -438,42 +639,68 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = p.K / BK;  // >= 8: K is a multiple of 256
+  const int nk = p.K / BK;  // >= 2: K is a multiple of 256
+  // Per stage k (slot k % 2; fragments of its first K-step already in
+  // registers): read K-step s+1 while the MFMAs of K-step s run; after the
+  // last reads of stage k, wait for stage k+1, sync (every wave's reads of
+  // stage k are then complete), refill slot k % 2 with stage k+2 and read
+  // stage k+1's first K-step while the last MFMAs of stage k run.
+  frag_t fa[2][4], fb[2][TN];
+  auto read_frags = [&](const unsigned char *st, int s, frag_t (&f_a)[4], frag_t (&f_b)[TN]) {
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of stage kt have landed once at most the loads of
-    // the stages issued after it are outstanding
-    if (kt + NST - 2 < nk) wait_vmcnt<2 * NLD * (NST - 2)>();
-    else if (kt + 1 < nk) wait_vmcnt<2 * NLD>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // every wave's loads of stage kt landed; stage kt-1 is free
-    if (kt + NST - 1 < nk) issue(kt + NST - 1);
-    const unsigned char *st = lds + (kt % NST) * STAGE;
-    frag_t fa[2][4], fb[2][TN];
+    for (int i = 0; i < 4; ++i) f_a[i] = *reinterpret_cast<const frag_t *>(st + frag_off(rA, i, s));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const frag_t *>(st + frag_off(rA, i, 0));
+    for (int j = 0; j < TN; ++j) f_b[j] = *reinterpret_cast<const frag_t *>(st + SLICE + frag_off(rB, j, s));
+  };
+  auto mfmas = [&](const frag_t (&f_a)[4], const frag_t (&f_b)[TN]) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = *reinterpret_cast<const frag_t *>(st + SLICE + frag_off(rB, j, 0));
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (s + 1 < S) {
+      for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(f_a[i], f_b[j], acc[i][j]);
+  };
+  // interleave the fragment reads issued next to an MFMA group with it
+  auto interleave = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[(s + 1) & 1][i] = *reinterpret_cast<const frag_t *>(st + frag_off(rA, i, s + 1));
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          fb[(s + 1) & 1][j] = *reinterpret_cast<const frag_t *>(st + SLICE + frag_off(rB, j, s + 1));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+    for (int q = 0; q < 4 + TN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
+  };
+  static_assert(NST == 2, "the pipeline below is a double buffer");
+  issue(0);
+  issue(1);
+  wait_vmcnt<2 * NLD>();  // stage 0 landed (stage 1 may be in flight)
+  __syncthreads();
+  read_frags(lds, 0, fa[0], fb[0]);
+  // all stages but the last (uniform control flow keeps the LDS wait counts exact)
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const unsigned char *st = lds + (kt & 1) * STAGE;
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s) {
+      read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      mfmas(fa[s & 1], fb[s & 1]);
+      interleave();
+    }
+    wait_vmcnt<0>();  // stage kt+1 landed
+    __syncthreads();  // every wave's stage kt+1 landed and its reads of stage kt are done
+    if (kt + 2 < nk) issue(kt + 2);
+    read_frags(lds + ((kt + 1) & 1) * STAGE, 0, fa[S & 1], fb[S & 1]);
+    mfmas(fa[(S - 1) & 1], fb[(S - 1) & 1]);
+    interleave();
+  }
+  {  // last stage
+    const unsigned char *st = lds + ((nk - 1) & 1) * STAGE;
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s) {
+      read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      mfmas(fa[s & 1], fb[s & 1]);
+    }
+    mfmas(fa[(S - 1) & 1], fb[(S - 1) & 1]);
   }
 
-  // ---- fp32 epilogue (same contract as gemm_nt_kernel) ----
-  run_epilogue<T, SYM, 4, TN>(p, acc, g, SYM && (tm == tn), tm * 256 + wm * 128, tn * 256 + wn * WN, lane);
+  // ---- fp32 epilogue (same contract as gemm_nt_kernel), staged in LDS ----
+  __syncthreads();  // all waves are done with the operand stages
+  staged_epilogue<T, SYM, NW, TN, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
 }
 
 int tile_m(int cfg) { return cfg == kTile256 ? 256 : 128; }
@@ -507,7 +734,7 @@ static hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-constexpr int kWaves256 = 8;
+constexpr int kWaves256 = 4;
 
 template <int DT, bool SYM>
 static hipError_t launch_256(const GemmArgs &a, hipStream_t s) {
