@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -94,8 +95,18 @@ nsg_status_t validate_shape(int64_t G, int64_t R, int64_t C) {
 
 // Tile configuration from (n, m, dtype) only — never from G — so a matrix's
 // arithmetic is the same in any bucket.
+// NSG_TILE=128|256 in the environment forces a tile configuration (a
+// debugging and tuning aid; it applies to every matrix alike).
 int choose_cfg(int64_t np, int64_t mp, int dt) {
   (void)mp;
+  static const int forced = [] {
+    const char *e = std::getenv("NSG_TILE");
+    if (e == nullptr) return 0;
+    const int v = std::atoi(e);
+    return (v == 128 || v == 256) ? v : 0;
+  }();
+  if (forced == 128) return kTile128;
+  if (forced == 256) return kTile256;
   if (dt == NSG_F32) return kTile128;  // debug path
   return np >= 512 ? kTile256 : kTile128;
 }

@@ -780,8 +780,14 @@ __device__ __forceinline__ float block_sum_256(float v, float *red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-template <typename TI>
+// Each thread owns elements start + 256 V k + V t + v (v < V, V = 16 bytes of
+// input); it sums their squares in that order whether it reads them with one
+// 16-byte load (aligned input) or V scalar loads, so the result never depends
+// on the input's alignment.
+template <typename TI, bool VEC>
 __global__ void __launch_bounds__(256) norm_reduce_kernel(const NormReduceArgs p) {
+  constexpr int V = 16 / (int)sizeof(TI);
+  typedef TI vec_t __attribute__((ext_vector_type(V)));
   __shared__ float red[4];
   const int g = blockIdx.y;
   const int64_t start = (int64_t)blockIdx.x * kNormChunk;
@@ -789,9 +795,20 @@ __global__ void __launch_bounds__(256) norm_reduce_kernel(const NormReduceArgs p
   if (end > p.elems) end = p.elems;
   const TI *in = reinterpret_cast<const TI *>(p.in) + (size_t)g * p.elems;
   float s = 0.f;
-  for (int64_t i = start + threadIdx.x; i < end; i += 256) {
-    const float v = to_f32(in[i]);
-    s = fmaf(v, v, s);
+  for (int64_t i = start + (int64_t)threadIdx.x * V; i < end; i += 256 * V) {
+    if (VEC && i + V <= end) {
+      const vec_t x = *reinterpret_cast<const vec_t *>(in + i);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float f = to_f32(x[v]);
+        s = fmaf(f, f, s);
+      }
+    } else {
+      for (int v = 0; v < V && i + v < end; ++v) {
+        const float f = to_f32(in[i + v]);
+        s = fmaf(f, f, s);
+      }
+    }
   }
   s = block_sum_256(s, red);
   if (threadIdx.x == 0) p.partials[(size_t)g * p.nchunks + blockIdx.x] = s;
@@ -800,21 +817,34 @@ __global__ void __launch_bounds__(256) norm_reduce_kernel(const NormReduceArgs p
 hipError_t launch_norm_reduce(const NormReduceArgs &a, hipStream_t s) {
   if (a.batch == 0 || a.elems == 0) return hipSuccess;
   dim3 grid((unsigned)a.nchunks, (unsigned)a.batch), block(256);
+  const size_t es = a.in_dtype == NSG_F32 ? 4 : 2;
+  const bool vec = (reinterpret_cast<uintptr_t>(a.in) % 16 == 0) && ((size_t)a.elems * es) % 16 == 0;
+#define NSG_RED(TI) \
+  if (vec) hipLaunchKernelGGL((norm_reduce_kernel<TI, true>), grid, block, 0, s, a); \
+  else hipLaunchKernelGGL((norm_reduce_kernel<TI, false>), grid, block, 0, s, a)
   switch (a.in_dtype) {
-    case NSG_F16: hipLaunchKernelGGL(norm_reduce_kernel<_Float16>, grid, block, 0, s, a); break;
-    case NSG_BF16: hipLaunchKernelGGL(norm_reduce_kernel<__bf16>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(norm_reduce_kernel<float>, grid, block, 0, s, a); break;
+    case NSG_F16: NSG_RED(_Float16); break;
+    case NSG_BF16: NSG_RED(__bf16); break;
+    default: NSG_RED(float); break;
   }
+#undef NSG_RED
   return hipGetLastError();
 }
 
 // Scale by an exact power of two, cast, and write both layouts through a
 // 64x64 LDS tile.  Every block recomputes the norm from the partial sums in
-// the same fixed order, so all blocks of a matrix agree bit for bit.
-template <typename TI, typename TO>
+// the same fixed order, so all blocks of a matrix agree bit for bit.  Each
+// thread moves 16 consecutive elements of a row: one or two 16-byte loads when
+// the input rows allow it (VEC), else scalar loads; the same values either
+// way.  Outputs (workspace, 128-byte-aligned pitches) use 16-byte stores.
+template <typename TI, typename TO, bool VEC>
 __global__ void __launch_bounds__(256) scale_cast_transpose_kernel(const ScaleArgs p) {
   __shared__ float tile[64][65];
   __shared__ float red[4];
+  constexpr int VI = 16 / (int)sizeof(TI);
+  constexpr int VO = 16 / (int)sizeof(TO);
+  typedef TI vin_t __attribute__((ext_vector_type(VI)));
+  typedef TO vout_t __attribute__((ext_vector_type(VO)));
   const int g = blockIdx.z;
   const int tid = threadIdx.x;
   float s = 0.f;
@@ -830,42 +860,71 @@ __global__ void __launch_bounds__(256) scale_cast_transpose_kernel(const ScaleAr
   }
   const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 64;
   const TI *in = reinterpret_cast<const TI *>(p.in) + (size_t)g * (size_t)(p.R * p.C);
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int idx = it * 256 + tid;
-    const int a = idx >> 6, b = idx & 63;
-    float v = 0.f;
-    if (a0 + a < p.R && b0 + b < p.C) v = to_f32(in[(size_t)(a0 + a) * p.C + (b0 + b)]);
-    tile[a][b] = ldexpf(v, e);
+  // load: thread -> row tid / 4, columns 16 (tid % 4) .. + 15
+  {
+    const int a = tid >> 2, bb = (tid & 3) * 16;
+    const int row = a0 + a, col = b0 + bb;
+    float v[16];
+    if (VEC && row < p.R && col + 16 <= p.C) {
+      const TI *src = in + (size_t)row * p.C + col;
+#pragma unroll
+      for (int u = 0; u < 16 / VI; ++u) {
+        const vin_t x = *reinterpret_cast<const vin_t *>(src + u * VI);
+#pragma unroll
+        for (int q = 0; q < VI; ++q) v[u * VI + q] = to_f32(x[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        v[q] = (row < p.R && col + q < p.C) ? to_f32(in[(size_t)row * p.C + col + q]) : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) tile[a][bb + q] = ldexpf(v[q], e);
   }
   __syncthreads();
   TO *same = reinterpret_cast<TO *>(p.same) + (size_t)g * p.s_same;
   TO *swp = reinterpret_cast<TO *>(p.swap) + (size_t)g * p.s_swap;
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int idx = it * 256 + tid;
-    const int a = idx >> 6, b = idx & 63;
-    same[(size_t)(a0 + a) * p.ld_same + (b0 + b)] = cvt<TO>(tile[a][b]);
-    swp[(size_t)(b0 + a) * p.ld_swap + (a0 + b)] = cvt<TO>(tile[b][a]);
+  {
+    const int a = tid >> 2, bb = (tid & 3) * 16;
+    // same layout: row a, columns bb .. bb + 15
+    TO *dst = same + (size_t)(a0 + a) * p.ld_same + (b0 + bb);
+#pragma unroll
+    for (int u = 0; u < 16 / VO; ++u) {
+      vout_t w;
+#pragma unroll
+      for (int q = 0; q < VO; ++q) w[q] = cvt<TO>(tile[a][bb + u * VO + q]);
+      *reinterpret_cast<vout_t *>(dst + u * VO) = w;
+    }
+    // transposed: output row (b0 + a) = input column a, input rows bb .. bb + 15
+    TO *dst2 = swp + (size_t)(b0 + a) * p.ld_swap + (a0 + bb);
+#pragma unroll
+    for (int u = 0; u < 16 / VO; ++u) {
+      vout_t w;
+#pragma unroll
+      for (int q = 0; q < VO; ++q) w[q] = cvt<TO>(tile[bb + u * VO + q][a]);
+      *reinterpret_cast<vout_t *>(dst2 + u * VO) = w;
+    }
   }
 }
 
-template <typename TI>
+template <typename TI, bool VEC>
 static void launch_scale_in(const ScaleArgs &a, dim3 grid, hipStream_t s) {
   switch (a.cdtype) {
-    case NSG_F16: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, _Float16>), grid, dim3(256), 0, s, a); break;
-    case NSG_BF16: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, __bf16>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, float>), grid, dim3(256), 0, s, a); break;
+    case NSG_F16: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, _Float16, VEC>), grid, dim3(256), 0, s, a); break;
+    case NSG_BF16: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, __bf16, VEC>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, float, VEC>), grid, dim3(256), 0, s, a); break;
   }
 }
 
 hipError_t launch_scale(const ScaleArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   dim3 grid((unsigned)(a.cols_p / 64), (unsigned)(a.rows_p / 64), (unsigned)a.batch);
+  const size_t es = a.in_dtype == NSG_F32 ? 4 : 2;
+  const bool vec = (reinterpret_cast<uintptr_t>(a.in) % 16 == 0) && ((size_t)a.C * es) % 16 == 0;
   switch (a.in_dtype) {
-    case NSG_F16: launch_scale_in<_Float16>(a, grid, s); break;
-    case NSG_BF16: launch_scale_in<__bf16>(a, grid, s); break;
-    default: launch_scale_in<float>(a, grid, s); break;
+    case NSG_F16: vec ? launch_scale_in<_Float16, true>(a, grid, s) : launch_scale_in<_Float16, false>(a, grid, s); break;
+    case NSG_BF16: vec ? launch_scale_in<__bf16, true>(a, grid, s) : launch_scale_in<__bf16, false>(a, grid, s); break;
+    default: vec ? launch_scale_in<float, true>(a, grid, s) : launch_scale_in<float, false>(a, grid, s); break;
   }
   return hipGetLastError();
 }
