@@ -1,6 +1,8 @@
 """Benchmark: batched Gram Newton–Schulz on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --calibrate-copy ...          (under rocprofv3 --pmc)
+    python bench.py --ingest-pmc FETCH.csv WRITE.csv [--workload NAME]
 
 One step = one ns_orthogonalize call over the whole bucket (normalize, every
 GEMM of Algorithm 3 or 1, output), inputs resident in HBM.  Prints one JSON
@@ -47,6 +49,63 @@ def algorithmic_flops(entry, G):
     return 0.0
 
 
+# Device kernel symbol -> the library's launch kind (the timing label).
+def kernel_kind(symbol: str):
+    if "copy_kernel" in symbol:
+        return "copy"
+    if "gemm256_kernel" in symbol or "gemm_nt_kernel" in symbol:
+        return "gemm_nt_sym" if ", true" in symbol else "gemm_nt"
+    if "norm_reduce_kernel" in symbol:
+        return "norm_reduce"
+    if "scale_cast_transpose_kernel" in symbol:
+        return "scale_cast_transpose"
+    return None
+
+
+COPY_BYTES = 1 << 30   # the calibration copy: 1 GiB read, 1 GiB written
+
+
+def read_counter_csv(path, counter):
+    """{kind: [value per dispatch]} for one counter of a rocprofv3 --pmc run."""
+    import csv
+
+    out = {}
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            k = kernel_kind(row["Kernel_Name"])
+            if k is not None:
+                out.setdefault(k, []).append(float(row["Counter_Value"]))
+    return out
+
+
+def ingest_pmc(fetch_csv, write_csv, workload):
+    """HBM bytes per launch of each GEMM kind from FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch), each scaled so that the calibration copy of COPY_BYTES reads
+    and writes exactly COPY_BYTES; stored with the kernel-source hash so that a
+    later change of the kernels voids it."""
+    fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = read_counter_csv(write_csv, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (1024.0 * sum(fetch["copy"]) / len(fetch["copy"]))
+    w_scale = COPY_BYTES / (1024.0 * sum(write["copy"]) / len(write["copy"]))
+    ent = {}
+    for k in ("gemm_nt", "gemm_nt_sym", "norm_reduce", "scale_cast_transpose"):
+        if k not in fetch or k not in write:
+            continue
+        rd = 1024.0 * f_scale * sum(fetch[k]) / len(fetch[k])
+        wr = 1024.0 * w_scale * sum(write[k]) / len(write[k])
+        ent[k] = {"bytes_per_launch": rd + wr, "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+                  "dispatches": len(fetch[k]), "kernel_src": kernel_source_hash()}
+    tr = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    tr[workload] = dict(ent, calibration={"copy_bytes": COPY_BYTES, "fetch_scale": f_scale,
+                                          "write_scale": w_scale})
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(tr, fh, indent=1, sort_keys=True)
+    print(json.dumps(tr[workload]))
+
+
 def cpu_baseline(w, x_cpu, budget_s: float = 30.0):
     """The oracle as it stands, on a bounded sample: whole matrices of the bucket,
     stopping once the time budget is spent (at least one matrix)."""
@@ -82,7 +141,14 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run the library copy kernel over COPY_BYTES (byte-counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store traffic per launch from two rocprofv3 --pmc counter_collection.csv files")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; --gpus > 1 is not supported "
                                    "(matrices are independent: the bucket would be split across GPUs)"}))
@@ -108,6 +174,14 @@ def main():
     status = torch.zeros(w.G, dtype=torch.int32, device=dev)
     plan = nsg.plan(w.R, w.C, **kw)
     credited, executed = nsg.flops(w.R, w.C, **kw)
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            nsg.copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
