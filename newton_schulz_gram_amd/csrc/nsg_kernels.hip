@@ -18,8 +18,13 @@
 
 #include <cfloat>
 #include <cstdint>
+#include <type_traits>
 
 #include "nsg_internal.h"
+
+#ifndef NSG_PF_AHEAD
+#define NSG_PF_AHEAD 2
+#endif
 
 namespace nsg {
 
@@ -344,8 +349,21 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
+// 4-byte load per lane from its own 64-bit address into LDS at m0 + 4 lane:
+// used only to pull lines into the caches ahead of the direct loads.
+__device__ __forceinline__ void lds_touch4(const void *addr, const void *lds) {
+  const unsigned m0v = (unsigned)(size_t)(lds_ptr_t)lds;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(m0v) : "memory");
+}
+// All of this wave's LDS reads have returned their data.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier that the compiler may not move memory accesses across and
+// that implies no wait on outstanding loads (the callers wait explicitly).
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 constexpr int kStages256 = 2;
+// stages between a prefetched slice and its direct load
+constexpr int kPrefetchAhead = NSG_PF_AHEAD;
 
 // 16-byte vector of 8 16-bit values, or of 4 floats.
 template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_type(16 / sizeof(TO)))); };
@@ -555,7 +573,7 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
   constexpr int EPI_PITCH = 132;  // floats per staged column (128 rows + 4)
   constexpr int EPI_BYTES = 256 * EPI_PITCH * 4;
   constexpr int LDS_BYTES = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES + 256];  // + prefetch sink
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -612,15 +630,16 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
     offA[i] = (unsigned)((row * (int)p.lda + chunk * CE) * ES);
     offB[i] = (unsigned)((row * (int)p.ldb + chunk * CE) * ES);
   }
-  auto issue = [&](int kt) {
-    unsigned char *st = lds + (kt % NST) * STAGE;
-    const T *a = gA + (size_t)kt * BK;
-    const T *b = gB + (size_t)kt * BK;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      lds_dma16(a, offA[i], st + (wave + NW * i) * 1024);
-      lds_dma16(b, offB[i], st + SLICE + (wave + NW * i) * 1024);
-    }
+  // Cache prefetch (wave 0 only): one 4-byte touch per row for an eighth of
+  // the rows of each operand panel, kPrefetchAhead stages ahead of the direct
+  // loads.  The tiles that share a panel (neighbours in the grouped order)
+  // touch different eighths, so together they bring whole slices from HBM
+  // into the last-level cache and L2 before any of them needs them.
+  const int nk = p.K / BK;  // >= 2: K is a multiple of 256
+  const T *pf_ptr = lane < 32 ? gA + (size_t)((tn & 7) + 8 * lane) * p.lda
+                              : gB + (size_t)((tm & 7) + 8 * (lane - 32)) * p.ldb;
+  auto prefetch = [&](int kt) {
+    if (wave == 0) lds_touch4(pf_ptr + (size_t)(kt < nk ? kt : nk - 1) * BK, lds + LDS_BYTES);
   };
 
   // ---- fragment reads: lane l reads row (block row + l%32) at K element
@@ -639,66 +658,92 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = p.K / BK;  // >= 2: K is a multiple of 256
-  // Per stage k (slot k % 2; fragments of its first K-step already in
-  // registers): read K-step s+1 while the MFMAs of K-step s run; after the
-  // last reads of stage k, wait for stage k+1, sync (every wave's reads of
-  // stage k are then complete), refill slot k % 2 with stage k+2 and read
-  // stage k+1's first K-step while the last MFMAs of stage k run.
-  frag_t fa[2][4], fb[2][TN];
-  auto read_frags = [&](const unsigned char *st, int s, frag_t (&f_a)[4], frag_t (&f_b)[TN]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f_a[i] = *reinterpret_cast<const frag_t *>(st + frag_off(rA, i, s));
-#pragma unroll
-    for (int j = 0; j < TN; ++j) f_b[j] = *reinterpret_cast<const frag_t *>(st + SLICE + frag_off(rB, j, s));
-  };
-  auto mfmas = [&](const frag_t (&f_a)[4], const frag_t (&f_b)[TN]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(f_a[i], f_b[j], acc[i][j]);
-  };
-  // interleave the fragment reads issued next to an MFMA group with it
-  auto interleave = [&]() {
-#pragma unroll
-    for (int q = 0; q < 4 + TN; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
-  };
+  // Pipeline over stages k (slot k % 2).  K-step s of a stage runs its
+  // 4 x TN MFMAs while the fragments of K-step s+1 are read, one read next to
+  // each of the first 4 + TN MFMAs.  Once every wave holds the last K-step of
+  // stage k in registers (barrier A, halfway through K-step S-2), slot k % 2
+  // is refilled with stage k+2.  The 2 NLD direct loads of a stage are spread
+  // at one per two MFMAs over the rest of stage k and K-step 0 of stage k+1,
+  // so the address unit never queues a wave's MFMA issue behind a burst of
+  // loads.  Barrier B (after K-step S-2) publishes stage k+1, whose loads all
+  // left one stage earlier.
   static_assert(NST == 2, "the pipeline below is a double buffer");
-  issue(0);
-  issue(1);
-  wait_vmcnt<2 * NLD>();  // stage 0 landed (stage 1 may be in flight)
+  static_assert(S >= 4 && S % 2 == 0, "K-steps per stage");
+  constexpr int NQ = 2 * NLD;                  // direct-load instructions per wave per stage
+  constexpr int Q1 = TN, Q2 = 2 * TN, Q3 = NQ - Q1 - Q2;
+  static_assert(Q3 >= 0 && Q3 <= 2 * TN, "load spread");
+  auto dma_q = [&](int kt, int slot, int q) {  // q-th load: pair q / 2, operand q % 2
+    unsigned char *st = lds + slot * STAGE;
+    const int i = q >> 1;
+    if (q & 1) lds_dma16(gB + (size_t)kt * BK, offB[i], st + SLICE + (wave + NW * i) * 1024);
+    else lds_dma16(gA + (size_t)kt * BK, offA[i], st + (wave + NW * i) * 1024);
+  };
+  frag_t fa[2][4], fb[2][TN];
+  const std::integral_constant<bool, true> kRd;
+  const std::integral_constant<bool, false> kNoRd;
+  // MFMAs of rows i0 .. i1-1 of one K-step; next to MFMA m the m-th fragment
+  // read of K-step rs of stage rst (when `reads` is true) and, after every second
+  // MFMA, the next of `nq` loads (from q0) of stage dk into slot dslot.
+  auto kstep = [&](const frag_t (&f_a)[4], const frag_t (&f_b)[TN], int i0, int i1, auto reads,
+                   const unsigned char *rst, int rs, frag_t (&n_a)[4], frag_t (&n_b)[TN],
+                   int dk, int dslot, int q0, int nq) {
+    constexpr bool RD = decltype(reads)::value;
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int m = (i - i0) * TN + j;
+        acc[i][j] = MF::mma(f_a[i], f_b[j], acc[i][j]);
+        if (RD && m < 4 + TN) {
+          if (m < 4) n_a[m] = *reinterpret_cast<const frag_t *>(rst + frag_off(rA, m, rs));
+          else n_b[m - 4] = *reinterpret_cast<const frag_t *>(rst + SLICE + frag_off(rB, m - 4, rs));
+        }
+        if ((m & 1) && (m >> 1) < nq) dma_q(dk, dslot, q0 + (m >> 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) dma_q(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < Q1 + Q2; ++q) dma_q(1, 1, q);
+  wait_vmcnt<Q1 + Q2>();  // stage 0 landed
   __syncthreads();
-  read_frags(lds, 0, fa[0], fb[0]);
-  // all stages but the last (uniform control flow keeps the LDS wait counts exact)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const frag_t *>(lds + frag_off(rA, i, 0));
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb[0][j] = *reinterpret_cast<const frag_t *>(lds + SLICE + frag_off(rB, j, 0));
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const unsigned char *st = lds + (kt & 1) * STAGE;
+    const unsigned char *nst = lds + ((kt + 1) & 1) * STAGE;
+    // past the end: stage nk-1 again, into the slot that is not read any
+    // more, so the wait counts stay uniform
+    const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+    kstep(fa[0], fb[0], 0, 4, kRd, st, 1, fa[1], fb[1], kt + 1, (kt + 1) & 1, Q1 + Q2, Q3);
+    prefetch(kt + 2 + kPrefetchAhead);
 #pragma unroll
-    for (int s = 0; s + 1 < S; ++s) {
-      read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      mfmas(fa[s & 1], fb[s & 1]);
-      interleave();
-    }
-    wait_vmcnt<0>();  // stage kt+1 landed
-    __syncthreads();  // every wave's stage kt+1 landed and its reads of stage kt are done
-    if (kt + 2 < nk) issue(kt + 2);
-    read_frags(lds + ((kt + 1) & 1) * STAGE, 0, fa[S & 1], fb[S & 1]);
-    mfmas(fa[(S - 1) & 1], fb[(S - 1) & 1]);
-    interleave();
+    for (int s = 1; s + 2 < S; ++s)
+      kstep(fa[s & 1], fb[s & 1], 0, 4, kRd, st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1], 0, 0, 0, 0);
+    kstep(fa[(S - 2) & 1], fb[(S - 2) & 1], 0, 2, kRd, st, S - 1, fa[(S - 1) & 1], fb[(S - 1) & 1], 0, 0, 0, 0);
+    wait_lgkmcnt0();  // this wave's reads of stage kt are in registers
+    raw_barrier();    // A: ... and every other wave's: slot kt % 2 is free
+    kstep(fa[(S - 2) & 1], fb[(S - 2) & 1], 2, 4, kNoRd, st, 0, fa[0], fb[0], kn, kt & 1, 0, Q1);
+    // this wave's loads of stage kt+1 landed (the first loads of stage kn and
+    // wave 0's last prefetch may be in flight)
+    if (wave == 0) wait_vmcnt<Q1 + 1>();
+    else wait_vmcnt<Q1>();
+    raw_barrier();  // B: every wave's loads of stage kt+1 landed
+    kstep(fa[(S - 1) & 1], fb[(S - 1) & 1], 0, 4, kRd, nst, 0, fa[0], fb[0], kn, kt & 1, Q1, Q2);
   }
   {  // last stage
     const unsigned char *st = lds + ((nk - 1) & 1) * STAGE;
 #pragma unroll
-    for (int s = 0; s + 1 < S; ++s) {
-      read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      mfmas(fa[s & 1], fb[s & 1]);
-    }
-    mfmas(fa[(S - 1) & 1], fb[(S - 1) & 1]);
+    for (int s = 0; s + 1 < S; ++s)
+      kstep(fa[s & 1], fb[s & 1], 0, 4, kRd, st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1], 0, 0, 0, 0);
+    kstep(fa[(S - 1) & 1], fb[(S - 1) & 1], 0, 4, kNoRd, st, 0, fa[0], fb[0], 0, 0, 0, 0);
   }
 
   // ---- fp32 epilogue (same contract as gemm_nt_kernel), staged in LDS ----
+  wait_vmcnt<0>();  // the last (unused) refill has landed
   __syncthreads();  // all waves are done with the operand stages
   staged_epilogue<T, SYM, NW, TN, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
 }
