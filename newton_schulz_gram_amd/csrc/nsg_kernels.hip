@@ -368,23 +368,25 @@ constexpr int kPrefetchAhead = NSG_PF_AHEAD;
 // 16-byte vector of 8 16-bit values, or of 4 floats.
 template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_type(16 / sizeof(TO)))); };
 
-// Epilogue of a 256x256 tile through LDS, in two passes of 128 rows.
-//   A: the waves owning the pass's rows write their fp32 accumulators into
-//      LDS, column-major (column c of the tile at c * PITCH floats), one
-//      16-byte write per 4 consecutive rows.
-//   B1: every thread takes 8 rows x 8 columns per step (a wave covers 8 rows
-//      x 64 columns: whole 128-byte lines of the row-major operands), forms
-//      v = alpha' acc + beta' Cin (0 outside the valid corner), writes v back
-//      to LDS and stores out0 (and out2 = v + diag I) row-major.
-//   B2: every thread takes 8 consecutive rows of one column (4 columns per
-//      wave step = 4 whole output rows of 256 bytes) and stores the transposed
-//      copy: the mirror (j, i) of a symmetric product, or out1 = V^T.
+// Epilogue of a 256x256 tile through LDS, in two passes of 128 rows.  The
+// fp32 tile is staged column-major (column c at c * PITCH floats, PITCH =
+// 132: A and B2 are free of LDS bank conflicts, B1's reads are 2-way).
+//   A: the waves owning the pass's rows write their accumulators, one
+//      16-byte write per 4 consecutive rows of a column.
+//   B1: a thread takes 1 row x 8 columns per step (a wave: 16 rows x 32
+//      columns, 64-byte row segments), forms v = alpha' acc + beta' Cin (0
+//      outside the valid corner) and stores out0 (and out2 = v + diag I)
+//      row-major; v goes back to LDS only when a transposed copy follows.
+//   B2: a thread takes 8 consecutive rows of one column (a wave: 64 rows x 8
+//      columns, 128-byte segments of 8 output rows) and stores the
+//      transposed copy: the mirror (j, i) of a symmetric product, or out1.
 // Inside a diagonal tile of a symmetric product only the lower half is
-// stored, to both places, so the output is exactly symmetric.
+// stored, to both places, so the output is exactly symmetric.  The
+// non-finite check of out0 runs only when a status array is given.
 template <typename T, typename TO, bool SYM, int NW, int TN, int PITCH>
 __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x16 (&acc)[4][TN], float *lds, int g,
                                                   int tm, int tn, int wm, int wn, int lane, int tid) {
-  constexpr int NT = NW * 64;
+  static_assert(PITCH % 4 == 0, "16-byte staging writes");
   constexpr int WN = TN * 32;
   constexpr int VT = 16 / (int)sizeof(T);   // elements of T per 16 bytes
   constexpr int VO = 16 / (int)sizeof(TO);  // elements of TO per 16 bytes
@@ -399,7 +401,9 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
   T *o1 = p.out1 ? reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1 : nullptr;
   T *o2 = p.out2 ? reinterpret_cast<T *>(p.out2) + (size_t)g * p.s2 : nullptr;
   const bool pad0 = p.out0_pad != 0;
+  const bool chk = p.status != nullptr;
   const bool diag_tile = SYM && (tm == tn);
+  const bool transposed = SYM || o1 != nullptr;  // B2 runs
   // 16-byte row stores need the row pitch and base of out0 to allow them
   const bool vec0 = o0 != nullptr && (p.ld0 % VO) == 0 && ((reinterpret_cast<uintptr_t>(o0) & 15) == 0);
   const int wave = tid >> 6;
@@ -408,56 +412,61 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
   for (int pass = 0; pass < 2; ++pass) {
     const int grow0 = tm * 256 + pass * 128;  // global row of staged row 0
     const int gcol0 = tn * 256;
+    const bool interior = grow0 + 128 <= p.Mv && gcol0 + 256 <= p.Nv;
     // ---- A: accumulators -> LDS ----
     if (wm == pass) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int c = wn * WN + j * 32 + (lane & 31);
+          float *col = lds + (wn * WN + j * 32 + (lane & 31)) * PITCH + i * 32 + 4 * (lane >> 5);
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int r = i * 32 + 8 * r4 + 4 * (lane >> 5);
-            float4 v4 = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
-                                    acc[i][j][4 * r4 + 3]);
-            *reinterpret_cast<float4 *>(lds + c * PITCH + r) = v4;
-          }
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<float4 *>(col + 8 * r4) = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                                                    acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
         }
     }
     __syncthreads();
     // ---- B1: row orientation ----
     {
-      const int rs = lane & 7, cgl = lane >> 3;  // 8 rows x 8 column groups per wave step
+      const int rs = lane & 15, cg = lane >> 4;
 #pragma unroll 1
-      for (int it = wave; it < 16 * 4; it += NW) {
-        const int rb = (it >> 2) * 8, cb = (it & 3) * 64;
-        const int r = rb + rs, c = cb + cgl * 8;
+      for (int it = wave; it < 64; it += NW) {
+        const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
         const int row = grow0 + r, col = gcol0 + c;
+        float *src = lds + c * PITCH + r;
         float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = alpha * lds[(c + q) * PITCH + r];
+        for (int q = 0; q < 8; ++q) v[q] = alpha * src[q * PITCH];
         if (cin != nullptr) {
-          typename Vec16<T>::type cv[8 / VT > 0 ? 8 / VT : 1];
-          const T *src = cin + (size_t)row * p.ldc + col;
+          const T *cp = cin + (size_t)row * p.ldc + col;
 #pragma unroll
-          for (int u = 0; u < 8 / VT; ++u) cv[u] = *reinterpret_cast<const typename Vec16<T>::type *>(src + u * VT);
+          for (int u = 0; u < 8 / VT; ++u) {
+            const typename Vec16<T>::type cv = *reinterpret_cast<const typename Vec16<T>::type *>(cp + u * VT);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] += beta * (float)cv[q / VT][q % VT];
+            for (int q = 0; q < VT; ++q) v[u * VT + q] += beta * (float)cv[q];
+          }
         }
         const bool rv = row < p.Mv;
+        if (!interior) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (!(rv && col + q < p.Nv)) v[q] = 0.f;
+          for (int q = 0; q < 8; ++q)
+            if (!(rv && col + q < p.Nv)) v[q] = 0.f;
+        }
+        if (transposed) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) lds[(c + q) * PITCH + r] = v[q];
-        const bool all_valid = rv && col + 8 <= p.Nv;
+          for (int q = 0; q < 8; ++q) src[q * PITCH] = v[q];
+        }
+        const bool all_valid = interior || (rv && col + 8 <= p.Nv);
         if (o0 != nullptr) {
           TO h[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) h[q] = cvt<TO>(v[q]);
+          if (chk) {
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (rv && col + q < p.Nv) finite = finite && __builtin_isfinite((float)h[q]);
+            for (int q = 0; q < 8; ++q)
+              if (all_valid || (rv && col + q < p.Nv)) finite = finite && __builtin_isfinite((float)h[q]);
+          }
           TO *dst = o0 + (size_t)row * p.ld0 + col;
           if (vec0 && !diag_tile && (all_valid || pad0)) {
 #pragma unroll
@@ -496,45 +505,48 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
         }
       }
     }
-    __syncthreads();
-    // ---- B2: column orientation (transposed copy) ----
-    T *ot = SYM ? reinterpret_cast<T *>(o0) : o1;  // symmetric outputs are in the compute dtype
-    const int ldt = SYM ? (int)p.ld0 : (int)p.ld1;
+    if (transposed) {
+      __syncthreads();
+      // ---- B2: column orientation (transposed copy) ----
+      T *ot = SYM ? reinterpret_cast<T *>(o0) : o1;  // symmetric outputs are in the compute dtype
+      const int ldt = SYM ? (int)p.ld0 : (int)p.ld1;
+      const int rg = lane & 7, cc = lane >> 3;
 #pragma unroll 1
-    for (int k = 0; k < 2; ++k) {
-      T *dstbase = (k == 0) ? ot : (SYM ? o2 : nullptr);
-      const int ldk = (k == 0) ? ldt : (int)p.ld2;
-      if (dstbase == nullptr) continue;
-      const int rg = lane & 15, cl = lane >> 4;  // 16 groups of 8 rows x 4 columns per wave step
+      for (int k = 0; k < 2; ++k) {
+        T *dstbase = (k == 0) ? ot : (SYM ? o2 : nullptr);
+        const int ldk = (k == 0) ? ldt : (int)p.ld2;
+        if (dstbase == nullptr) continue;
 #pragma unroll 1
-      for (int it = wave; it < 64; it += NW) {
-        const int c = it * 4 + cl, r = rg * 8;
-        const int row = grow0 + r, col = gcol0 + c;
-        const float4 a4 = *reinterpret_cast<const float4 *>(lds + c * PITCH + r);
-        const float4 b4 = *reinterpret_cast<const float4 *>(lds + c * PITCH + r + 4);
-        const float v[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
-        T h[8];
+        for (int it = wave; it < 64; it += NW) {
+          const int r = (it >> 5) * 64 + rg * 8, c = (it & 31) * 8 + cc;
+          const int row = grow0 + r, col = gcol0 + c;
+          const float *src = lds + c * PITCH + r;
+          const float4 f0 = *reinterpret_cast<const float4 *>(src);
+          const float4 f1 = *reinterpret_cast<const float4 *>(src + 4);
+          const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+          T h[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) h[q] = cvt<T>(v[q]);
-        T *dst = dstbase + (size_t)col * ldk + row;
-        if (!diag_tile) {
+          for (int q = 0; q < 8; ++q) h[q] = cvt<T>(v[q]);
+          T *dst = dstbase + (size_t)col * ldk + row;
+          if (!diag_tile) {
 #pragma unroll
-          for (int u = 0; u < 8 / VT; ++u) {
-            typename Vec16<T>::type w;
+            for (int u = 0; u < 8 / VT; ++u) {
+              typename Vec16<T>::type w;
 #pragma unroll
-            for (int q = 0; q < VT; ++q) w[q] = h[u * VT + q];
-            *reinterpret_cast<typename Vec16<T>::type *>(dst + u * VT) = w;
+              for (int q = 0; q < VT; ++q) w[q] = h[u * VT + q];
+              *reinterpret_cast<typename Vec16<T>::type *>(dst + u * VT) = w;
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (row + q > col) dst[q] = h[q];
           }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (row + q > col) dst[q] = h[q];
         }
       }
     }
-    __syncthreads();  // LDS is rewritten by the next pass
+    if (pass == 0) __syncthreads();  // LDS is rewritten by the next pass
   }
-  if (p.status != nullptr && __ballot(!finite) != 0 && lane == 0) p.status[g] = 1;
+  if (chk && __ballot(!finite) != 0 && lane == 0) p.status[g] = 1;
 }
 
 template <typename T, bool SYM, int NW, int TN, int PITCH>
