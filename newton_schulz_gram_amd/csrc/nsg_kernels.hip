@@ -366,6 +366,12 @@ constexpr int kStages256 = 2;
 constexpr int kPrefetchAhead = NSG_PF_AHEAD;
 
 // 16-byte vector of 8 16-bit values, or of 4 floats.
+// Output stores of the GEMM epilogues are non-temporal: the tiles are not
+// read again by this kernel, and streaming them past the caches keeps the
+// shader clock up (cached stores of whole output tiles measured about 45%
+// slower on the general 4096 x 4096 products).
+template <typename V> __device__ __forceinline__ void st_stream(const V &v, V *p) { __builtin_nontemporal_store(v, p); }
+
 template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_type(16 / sizeof(TO)))); };
 
 // Epilogue of a 256x256 tile through LDS, in two passes of 128 rows.  The
@@ -430,22 +436,38 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
     // ---- B1: row orientation ----
     {
       const int rs = lane & 15, cg = lane >> 4;
+      constexpr int U = 4;  // steps whose LDS reads are issued together
 #pragma unroll 1
-      for (int it = wave; it < 64; it += NW) {
+      for (int k0 = 0; k0 < 64 / NW; k0 += U) {
+        float vv[U][8];
+        typename Vec16<T>::type cvv[U][8 / VT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int it = wave + NW * (k0 + u);
+          const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
+          const float *src = lds + c * PITCH + r;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) vv[u][q] = src[q * PITCH];
+          if (cin != nullptr) {
+            const T *cp = cin + (size_t)(grow0 + r) * p.ldc + (gcol0 + c);
+#pragma unroll
+            for (int e = 0; e < 8 / VT; ++e) cvv[u][e] = *reinterpret_cast<const typename Vec16<T>::type *>(cp + e * VT);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+        const int it = wave + NW * (k0 + u);
         const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
         const int row = grow0 + r, col = gcol0 + c;
         float *src = lds + c * PITCH + r;
         float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = alpha * src[q * PITCH];
+        for (int q = 0; q < 8; ++q) v[q] = alpha * vv[u][q];
         if (cin != nullptr) {
-          const T *cp = cin + (size_t)row * p.ldc + col;
 #pragma unroll
-          for (int u = 0; u < 8 / VT; ++u) {
-            const typename Vec16<T>::type cv = *reinterpret_cast<const typename Vec16<T>::type *>(cp + u * VT);
+          for (int e = 0; e < 8 / VT; ++e)
 #pragma unroll
-            for (int q = 0; q < VT; ++q) v[u * VT + q] += beta * (float)cv[q];
-          }
+            for (int q = 0; q < VT; ++q) v[e * VT + q] += beta * (float)cvv[u][e][q];
         }
         const bool rv = row < p.Mv;
         if (!interior) {
@@ -470,16 +492,16 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
           TO *dst = o0 + (size_t)row * p.ld0 + col;
           if (vec0 && !diag_tile && (all_valid || pad0)) {
 #pragma unroll
-            for (int u = 0; u < 8 / VO; ++u) {
+            for (int e = 0; e < 8 / VO; ++e) {
               typename Vec16<TO>::type w;
 #pragma unroll
-              for (int q = 0; q < VO; ++q) w[q] = h[u * VO + q];
-              *reinterpret_cast<typename Vec16<TO>::type *>(dst + u * VO) = w;
+              for (int q = 0; q < VO; ++q) w[q] = h[e * VO + q];
+              st_stream(w, reinterpret_cast<typename Vec16<TO>::type *>(dst + e * VO));
             }
           } else {
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-              if ((pad0 || (rv && col + q < p.Nv)) && (!diag_tile || row >= col + q)) dst[q] = h[q];
+              if ((pad0 || (rv && col + q < p.Nv)) && (!diag_tile || row >= col + q)) st_stream(h[q], dst + q);
           }
         }
         if constexpr (SYM) {
@@ -490,18 +512,19 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
             T *dst = o2 + (size_t)row * p.ld2 + col;
             if (!diag_tile) {
 #pragma unroll
-              for (int u = 0; u < 8 / VT; ++u) {
+              for (int e = 0; e < 8 / VT; ++e) {
                 typename Vec16<T>::type w;
 #pragma unroll
-                for (int q = 0; q < VT; ++q) w[q] = h[u * VT + q];
-                *reinterpret_cast<typename Vec16<T>::type *>(dst + u * VT) = w;
+                for (int q = 0; q < VT; ++q) w[q] = h[e * VT + q];
+                st_stream(w, reinterpret_cast<typename Vec16<T>::type *>(dst + e * VT));
               }
             } else {
 #pragma unroll
               for (int q = 0; q < 8; ++q)
-                if (row >= col + q) dst[q] = h[q];
+                if (row >= col + q) st_stream(h[q], dst + q);
             }
           }
+        }
         }
       }
     }
@@ -516,7 +539,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
         T *dstbase = (k == 0) ? ot : (SYM ? o2 : nullptr);
         const int ldk = (k == 0) ? ldt : (int)p.ld2;
         if (dstbase == nullptr) continue;
-#pragma unroll 1
+#pragma unroll 4
         for (int it = wave; it < 64; it += NW) {
           const int r = (it >> 5) * 64 + rg * 8, c = (it & 31) * 8 + cc;
           const int row = grow0 + r, col = gcol0 + c;
@@ -534,12 +557,12 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
               typename Vec16<T>::type w;
 #pragma unroll
               for (int q = 0; q < VT; ++q) w[q] = h[u * VT + q];
-              *reinterpret_cast<typename Vec16<T>::type *>(dst + u * VT) = w;
+              st_stream(w, reinterpret_cast<typename Vec16<T>::type *>(dst + u * VT));
             }
           } else {
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-              if (row + q > col) dst[q] = h[q];
+              if (row + q > col) st_stream(h[q], dst + q);
           }
         }
       }
