@@ -33,7 +33,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("nsg_kernels.hip", "nsg_internal.h"):
+    for f in ("nsg_kernels.hip", "nsg_internal.h", "nsg_api.cpp"):  # kernels and the launch plan
         with open(os.path.join(ROOT, "newton_schulz_gram_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -140,6 +140,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--general-updates", action="store_true",
+                    help="run Q Z + a Q and R Z + a R as general products (default: symmetric kernel)")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run the library copy kernel over COPY_BYTES (byte-counter calibration)")
@@ -169,7 +171,7 @@ def main():
     x = x_cpu.to(dev)
     out = torch.empty_like(x)
     kw = dict(steps=w.steps, coeffs=w.coeffs, mode=w.mode, restart_after=w.restart_after,
-              safety=w.safety, compute_dtype=w.compute)
+              safety=w.safety, compute_dtype=w.compute, sym_updates=not args.general_updates)
     ws = torch.empty(nsg.workspace_size(w.G, w.R, w.C, **kw), dtype=torch.uint8, device=dev)
     status = torch.zeros(w.G, dtype=torch.int32, device=dev)
     plan = nsg.plan(w.R, w.C, **kw)
@@ -251,7 +253,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "G": w.G, "R": w.R, "C": w.C, "input_dtype": w.dtype,
                    "mode": w.mode, "steps": w.steps, "restart_after": w.restart_after,
-                   "safety": w.safety, "coeffs": list(w.coeffs), "accumulate": "f32"},
+                   "safety": w.safety, "coeffs": list(w.coeffs), "accumulate": "f32",
+                   "sym_updates": not args.general_updates},
         "effective_tflops": round(eff_tflops, 2),
         "pct_fp16_peak": round(100 * eff_tflops / PEAK_FP16_TFLOPS, 2),
         "executed_tflops": round(executed * w.G * args.steps / wall / 1e12, 2),

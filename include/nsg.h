@@ -86,10 +86,16 @@ typedef struct {
   float eps;              /* >= 0; Alg. 1: 1e-7 */
   int32_t compute_dtype;  /* nsg_dtype_t: F16 (Alg. 3), BF16 (Alg. 1), or F32
                              (debug path) */
+  int32_t sym_updates;    /* NSG_GRAM only.  1: the products Q Z + a Q and
+                             R Z + a R run on the symmetric kernel (lower
+                             triangle computed, mirrored), as the Dion3 paper's
+                             FLOP count in Section 4.1 assumes; Q, RZ and R are
+                             then exactly symmetric.  0: both run as general
+                             products.  Other values are an argument error. */
 } nsg_params_t;
 
 /* Fills *p with the defaults: steps 5, the Muon triple, NSG_GRAM,
- * restart_after 2, safety 1.05, eps 1e-7, fp16 compute.  The coefficient
+ * restart_after 2, safety 1.05, eps 1e-7, fp16 compute, sym_updates 1.  The coefficient
  * pointer refers to static storage inside the library. */
 void ns_default_params(nsg_params_t *p);
 

@@ -84,6 +84,7 @@ nsg_status_t validate_params(const nsg_params_t *p) {
   if (!(p->safety > 0.f) || !std::isfinite(p->safety)) return NSG_ERR_INVALID_ARG;
   if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return NSG_ERR_INVALID_ARG;
   if (!valid_dtype(p->compute_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (p->sym_updates != 0 && p->sym_updates != 1) return NSG_ERR_INVALID_ARG;
   return NSG_OK;
 }
 
@@ -226,6 +227,7 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     double xs = xs0;
     int xpow = 1;
     int Rb = kS0, Zb = kS1, Qcur = kNone, Qfree[2] = {kS2, kS3}, RZb = kS4, RZTb = kS5;
+    const bool symu = p->sym_updates != 0;
     bool r_scaled = true;  // R_true = 2^-2f R_stored (only R0)
     add_gemm(P, true, 0, "R0=XXt", kX0, kX0, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
              false);
@@ -251,18 +253,21 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
         Qcur = Qfree[0];
       } else {
         const int qn = (Qcur == Qfree[0]) ? Qfree[1] : Qfree[0];
-        add_gemm(P, false, t, "Q=QZ+aQ", Qcur, Zb, Qcur, qn, kNone, kNone, np, np, np, n, n, 1.0, a, 0.0, 0,
+        // Q Z = Q Z^T (Z is exactly symmetric); on the symmetric kernel the
+        // lower triangle is computed and mirrored
+        add_gemm(P, symu, t, "Q=QZ+aQ", Qcur, Zb, Qcur, qn, kNone, kNone, np, np, np, n, n, 1.0, a, 0.0, 0,
                  false);
         Qcur = qn;
       }
       const bool need_r = (t < P.T) && (t + 1 != P.restart);
       if (need_r) {
-        // RZ = R Z + a R (stored with R's scale), also written transposed
-        add_gemm(P, false, t, "RZ=RZ+aR", Rb, Zb, Rb, RZb, RZTb, kNone, np, np, np, n, n, 1.0, a, 0.0, 0,
-                 false);
+        // RZ = R Z + a R (stored with R's scale); as a general product it is
+        // also written transposed, as a symmetric one RZ^T = RZ exactly
+        add_gemm(P, symu, t, "RZ=RZ+aR", Rb, Zb, Rb, RZb, symu ? kNone : RZTb, kNone, np, np, np, n, n, 1.0,
+                 a, 0.0, 0, false);
         // R = Z RZ + a RZ : NT with B = RZ^T
-        add_gemm(P, true, t, "R=Z.RZ+aRZ", Zb, RZTb, RZb, Rb, kNone, kNone, np, np, np, n, n, rs, a * rs,
-                 0.0, 0, false);
+        add_gemm(P, true, t, "R=Z.RZ+aRZ", Zb, symu ? RZb : RZTb, RZb, Rb, kNone, kNone, np, np, np, n, n, rs,
+                 a * rs, 0.0, 0, false);
         r_scaled = false;
       }
     }
@@ -337,6 +342,7 @@ void ns_default_params(nsg_params_t *p) {
   p->safety = 1.05f;
   p->eps = 1e-7f;
   p->compute_dtype = NSG_F16;
+  p->sym_updates = 1;
 }
 
 const char *ns_status_string(nsg_status_t s) {

@@ -228,3 +228,59 @@ def test_single_matrix_2d_input():
     torch.cuda.synchronize()
     assert out.shape == (100, 300) and out.dtype == torch.bfloat16
     check(out.unsqueeze(0), oracle_of(x), "f16")
+
+
+# ---------------------------------------------------------------------------
+# General Q Z + a Q and R Z + a R (sym_updates=False; the default runs them
+# on the symmetric kernel): every conditioning class, the restart locations
+# and the full-size buckets
+# ---------------------------------------------------------------------------
+
+def test_general_updates_gpt2s_all_conditionings():
+    w = WORKLOADS["gpt2s_mlp_42x768x3072_f16"]
+    x = synth.make(w)
+    ref = oracle_of(x, safety=w.safety)
+    out = run(x, safety=w.safety, sym_updates=False)
+    rel, cos = metrics(out, ref)
+    worst = {}
+    for g in range(w.G):
+        c = conditioning_class_of(w.G, g)
+        worst[c] = max(worst.get(c, 0.0), float(rel[g]))
+    print("general updates per-class max rel error:", {k: round(v, 5) for k, v in worst.items()})
+    assert rel.max() <= HALF_REL, worst
+    assert cos.min() >= HALF_COS
+    for g in (0, 20, 41):
+        one = run(x[g:g + 1], safety=w.safety, sym_updates=False)
+        assert torch.equal(one[0], out[g])
+
+
+@pytest.mark.parametrize("compute", ["f32", "f16", "bf16"])
+def test_general_updates_single_128x512(compute):
+    x = synth.make(WORKLOADS["single_1x128x512_f32"])
+    ref = oracle_of(x, safety=1.0)
+    out = run(x, safety=1.0, compute_dtype=compute, sym_updates=False, out_dtype=torch.float32)
+    check(out, ref, compute, f"general updates {compute}")
+
+
+@pytest.mark.parametrize("restart_after", [0, 1, 3, 4])
+def test_general_updates_restart_locations(restart_after):
+    x = custom(2, 256, 1024, "f16", "gaussian", seed=23)
+    ref = oracle_of(x, restart_after=restart_after)
+    out = run(x, restart_after=restart_after, sym_updates=False)
+    check(out, ref, "f16", f"general updates restart {restart_after}")
+
+
+def test_general_updates_moe_and_llama7b_sampled():
+    w = WORKLOADS["moe_512x2048x512_f16"]
+    x = synth.make(w)
+    out = run(x, safety=w.safety, sym_updates=False)
+    idx = [0, 255, 511]
+    check(out[idx], oracle_of(x[idx], safety=w.safety), "f16", "moe general updates")
+    del x, out
+    w = WORKLOADS["llama7b_mlp_32x11008x4096_bf16"]
+    x = synth.make(w)
+    out = run(x, safety=w.safety, sym_updates=False)
+    rel, cos = check(out[:1], oracle_of(x[:1], safety=w.safety), "f16", "7b general updates")
+    print("7b general updates matrix 0: rel %.3e cos %.6f" % (rel[0], cos[0]))
+    one = run(x[7:8], safety=w.safety, sym_updates=False)
+    assert torch.equal(one[0], out[7])

@@ -43,6 +43,7 @@ def test_default_params():
     assert p.restart_after == 2 and abs(p.safety - 1.05) < 1e-6 and abs(p.eps - 1e-7) < 1e-12
     assert [p.coeffs[i] for i in range(3)] == list(nsg.MUON_COEFFS)
     assert p.compute_dtype == nsg.NSG_F16
+    assert p.sym_updates == 1
 
 
 def _call(G=2, R=64, C=128, in_dtype=0, out_dtype=0, ws_bytes=None, ws_ptr=1 << 20, **kw):
@@ -74,6 +75,15 @@ def _call(G=2, R=64, C=128, in_dtype=0, out_dtype=0, ws_bytes=None, ws_ptr=1 << 
 ])
 def test_validation_before_launch(kw, code):
     assert _call(**kw) == code
+
+
+def test_sym_updates_must_be_0_or_1():
+    p, keep = nsg.make_params()
+    p.sym_updates = 2
+    out = ctypes.c_size_t(0)
+    assert nsg.lib().ns_workspace_size(1, 64, 128, ctypes.byref(p), ctypes.byref(out)) == 1
+    p.sym_updates = 1
+    assert nsg.lib().ns_workspace_size(1, 64, 128, ctypes.byref(p), ctypes.byref(out)) == 0
 
 
 def test_empty_bucket_is_a_no_op():
@@ -147,3 +157,27 @@ def test_workspace_scales_with_bucket():
     b = nsg.workspace_size(32, 11008, 4096)
     assert 31 * a <= b <= 32 * a + 32 * 256
     assert a % 256 == 0 and b % 256 == 0
+
+
+def test_sym_updates_plan():
+    """Q Z + a Q and R Z + a R on the symmetric kernel: same launches and
+    credited FLOPs, lower-triangle tiles only, no transposed RZ buffer."""
+    base = nsg.plan(11008, 4096, sym_updates=False)
+    symp = nsg.plan(11008, 4096)
+    assert [e["label"] for e in base] == [e["label"] for e in symp]
+    for e0, e1 in zip(base, symp):
+        if e0["label"] in ("Q=QZ+aQ", "RZ=RZ+aR"):
+            assert e0["kernel"] == "gemm_nt" and e1["kernel"] == "gemm_nt_sym"
+            assert e1["flops"] == pytest.approx(e0["flops"] * 136 / 256)  # 16 x 16 tiles -> 136
+        else:
+            assert e0["kernel"] == e1["kernel"] and e0["flops"] == e1["flops"]
+    cr0, ex0 = nsg.flops(11008, 4096, sym_updates=False)
+    cr1, ex1 = nsg.flops(11008, 4096)
+    assert cr0 == cr1 and ex1 < ex0
+    assert ex1 == pytest.approx(sum(e["flops"] for e in symp))
+    # RZ^T is not kept: one n x n buffer less per matrix
+    w0 = nsg.workspace_size(1, 11008, 4096, sym_updates=False)
+    w1 = nsg.workspace_size(1, 11008, 4096)
+    assert w0 - w1 >= 4096 * 4096 * 2
+    # standard mode ignores it
+    assert [e["kernel"] for e in nsg.plan(4096, 4096)] == [e["kernel"] for e in nsg.plan(4096, 4096, sym_updates=False)]
