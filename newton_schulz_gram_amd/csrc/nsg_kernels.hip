@@ -434,7 +434,86 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
     }
     __syncthreads();
     // ---- B1: row orientation ----
-    {
+    // Fast path: the whole pass is inside the valid corner, out0 takes 16-byte
+    // stores, the tile is off the diagonal and no status is checked, so no
+    // step needs a mask.
+    const bool fast = interior && (o0 == nullptr || vec0) && !diag_tile && !chk;
+    if (fast) {
+      auto b1 = [&](auto hc, auto tr, auto o2c) {
+        constexpr bool HC = decltype(hc)::value, TR = decltype(tr)::value, O2 = decltype(o2c)::value;
+        const int rs = lane & 15, cg = lane >> 4;
+        constexpr int U = 4;
+#pragma unroll 1
+        for (int k0 = 0; k0 < 64 / NW; k0 += U) {
+          float vv[U][8];
+          typename Vec16<T>::type cvv[U][8 / VT];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int it = wave + NW * (k0 + u);
+            const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
+            const float *src = lds + c * PITCH + r;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) vv[u][q] = src[q * PITCH];
+            if constexpr (HC) {
+              const T *cp = cin + (size_t)(grow0 + r) * p.ldc + (gcol0 + c);
+#pragma unroll
+              for (int e = 0; e < 8 / VT; ++e)
+                cvv[u][e] = *reinterpret_cast<const typename Vec16<T>::type *>(cp + e * VT);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int it = wave + NW * (k0 + u);
+            const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
+            const size_t row = (size_t)(grow0 + r), col = (size_t)(gcol0 + c);
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = alpha * vv[u][q];
+            if constexpr (HC) {
+#pragma unroll
+              for (int e = 0; e < 8 / VT; ++e)
+#pragma unroll
+                for (int q = 0; q < VT; ++q) v[e * VT + q] += beta * (float)cvv[u][e][q];
+            }
+            if constexpr (TR) {
+              float *src = lds + c * PITCH + r;
+#pragma unroll
+              for (int q = 0; q < 8; ++q) src[q * PITCH] = v[q];
+            }
+            if (o0 != nullptr) {
+              TO *dst = o0 + row * p.ld0 + col;
+#pragma unroll
+              for (int e = 0; e < 8 / VO; ++e) {
+                typename Vec16<TO>::type w;
+#pragma unroll
+                for (int q = 0; q < VO; ++q) w[q] = cvt<TO>(v[e * VO + q]);
+                st_stream(w, reinterpret_cast<typename Vec16<TO>::type *>(dst + e * VO));
+              }
+            }
+            if constexpr (O2) {  // off the diagonal: out2 = v
+              T *dst = o2 + row * p.ld2 + col;
+#pragma unroll
+              for (int e = 0; e < 8 / VT; ++e) {
+                typename Vec16<T>::type w;
+#pragma unroll
+                for (int q = 0; q < VT; ++q) w[q] = cvt<T>(v[e * VT + q]);
+                st_stream(w, reinterpret_cast<typename Vec16<T>::type *>(dst + e * VT));
+              }
+            }
+          }
+        }
+      };
+      using TT = std::integral_constant<bool, true>;
+      using FF = std::integral_constant<bool, false>;
+      const bool has_o2 = SYM && o2 != nullptr;
+      if (cin != nullptr) {
+        if (transposed) { if (has_o2) b1(TT{}, TT{}, TT{}); else b1(TT{}, TT{}, FF{}); }
+        else b1(TT{}, FF{}, FF{});
+      } else {
+        if (transposed) { if (has_o2) b1(FF{}, TT{}, TT{}); else b1(FF{}, TT{}, FF{}); }
+        else b1(FF{}, FF{}, FF{});
+      }
+    } else {
       const int rs = lane & 15, cg = lane >> 4;
       constexpr int U = 4;  // steps whose LDS reads are issued together
 #pragma unroll 1
