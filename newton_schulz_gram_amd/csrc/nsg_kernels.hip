@@ -569,7 +569,11 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
               if (all_valid || (rv && col + q < p.Nv)) finite = finite && __builtin_isfinite((float)h[q]);
           }
           TO *dst = o0 + (size_t)row * p.ld0 + col;
-          if (vec0 && !diag_tile && (all_valid || pad0)) {
+          // in a diagonal tile a group of 8 is wholly below the diagonal
+          // (row >= col + 7), wholly above it (row < col: stored by the
+          // mirror) or straddles it (masked element stores)
+          if (diag_tile && row < col) {
+          } else if (vec0 && (!diag_tile || row >= col + 7) && (all_valid || pad0)) {
 #pragma unroll
             for (int e = 0; e < 8 / VO; ++e) {
               typename Vec16<TO>::type w;
@@ -589,7 +593,8 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
 #pragma unroll
             for (int q = 0; q < 8; ++q) h[q] = cvt<T>((row == col + q && rv) ? v[q] + p.diag : v[q]);
             T *dst = o2 + (size_t)row * p.ld2 + col;
-            if (!diag_tile) {
+            if (diag_tile && row < col) {
+            } else if (!diag_tile || row >= col + 7) {
 #pragma unroll
               for (int e = 0; e < 8 / VT; ++e) {
                 typename Vec16<T>::type w;
@@ -630,7 +635,10 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
 #pragma unroll
           for (int q = 0; q < 8; ++q) h[q] = cvt<T>(v[q]);
           T *dst = dstbase + (size_t)col * ldk + row;
-          if (!diag_tile) {
+          // diagonal tile: rows row..row+7 of column col go to the upper half
+          // only where row + q > col
+          if (diag_tile && row + 7 <= col) {
+          } else if (!diag_tile || row > col) {
 #pragma unroll
             for (int u = 0; u < 8 / VT; ++u) {
               typename Vec16<T>::type w;
