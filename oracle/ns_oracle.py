@@ -10,7 +10,7 @@ the "muon" kernel card, "How it works"):
 
   * ``normalize``      X <- X / (s (||X||_F + eps))              (Alg. 1 / Alg. 3 step 2)
   * ``standard_ns``    A = X X^T, B = b A + c A^2, X <- a X + B X (Alg. 1)
-  * ``gram_ns``        R = X X^T, Q = I, loop with one restart    (Alg. 3)
+  * ``gram_ns``        R = X X^T, Q = I, loop with restarts       (Alg. 3, App. B.2)
   * ``orthogonalize``  the bucket wrapper: transpose so the short side leads,
                        pick the mode (square -> standard), normalize, iterate,
                        transpose back.
@@ -79,9 +79,20 @@ def standard_ns(X: np.ndarray, coeffs, steps: int = 5) -> np.ndarray:
     return X
 
 
+def _restart_steps(steps: int, restart_after: int, restarts):
+    """Steps t at whose top the iteration restarts.  ``restarts`` (any
+    iterable of steps 2..T) overrides the single ``restart_after``."""
+    if restarts is not None:
+        rs = sorted(set(int(t) for t in restarts))
+        if any(t < 2 or t > steps for t in rs):
+            raise ValueError("restart steps must lie in 2..steps")
+        return rs
+    return [restart_after + 1] if 1 <= restart_after < steps else []
+
+
 def gram_ns(X: np.ndarray, coeffs, steps: int = 5, restart_after: int = 2,
-            gram_shift: float = 0.0) -> np.ndarray:
-    """Gram Newton–Schulz with one restart, on an already normalized X (n <= m).
+            gram_shift: float = 0.0, restarts=None) -> np.ndarray:
+    """Gram Newton–Schulz with restarts, on an already normalized X (n <= m).
 
     Dion3 paper, Section 4.2, Algorithm 3 (stabilized Gram NS), with the a*I
     terms kept out of Z as in Appendix B.2.3:
@@ -94,6 +105,8 @@ def gram_ns(X: np.ndarray, coeffs, steps: int = 5, restart_after: int = 2,
             R_t    <- Z_t (RZ)_t + a_t (RZ)_t
         return Q_T X
     restart_after = 0 (or >= T) gives Algorithm 2 without a restart.
+    ``restarts`` lists several restart steps: Appendix B.2 repeats the
+    restart to reach any X_T, and B.2.1 sweeps schedules with more than one.
 
     ``gram_shift`` subtracts shift*I each time a Gram matrix is formed, the
     simulated spurious eigenvalue of Appendix B.2.1 (there: 4e-4); 0 normally.
@@ -102,8 +115,9 @@ def gram_ns(X: np.ndarray, coeffs, steps: int = 5, restart_after: int = 2,
     I = np.eye(n)
     R = X @ X.T - gram_shift * I
     Q = I.copy()
+    at = _restart_steps(steps, restart_after, restarts)
     for t, (a, b, c) in enumerate(_coeff_list(coeffs, steps), start=1):
-        if restart_after >= 1 and t == restart_after + 1:
+        if t in at:
             X = Q @ X
             R = X @ X.T - gram_shift * I
             Q = I.copy()
@@ -135,7 +149,8 @@ def naive_gram_ns(X: np.ndarray, coeffs, steps: int = 5,
 
 
 def ns_matrix(Y: np.ndarray, steps: int, coeffs, mode: str = "gram",
-              restart_after: int = 2, safety: float = 1.0, eps: float = EPS) -> np.ndarray:
+              restart_after: int = 2, safety: float = 1.0, eps: float = EPS,
+              restarts=None) -> np.ndarray:
     """One R x C matrix: transpose so n <= m, normalize, iterate, transpose back.
 
     Transposition: Alg. 1 takes X in R^{n x m} with n <= m; the "muon" kernel
@@ -150,7 +165,7 @@ def ns_matrix(Y: np.ndarray, steps: int, coeffs, mode: str = "gram",
     if mode == "standard" or n == m:
         X = standard_ns(X, coeffs, steps)
     elif mode == "gram":
-        X = gram_ns(X, coeffs, steps, restart_after)
+        X = gram_ns(X, coeffs, steps, restart_after, restarts=restarts)
     else:
         raise ValueError(f"unknown mode {mode!r}")
     return X.T if tr else X
@@ -158,7 +173,7 @@ def ns_matrix(Y: np.ndarray, steps: int, coeffs, mode: str = "gram",
 
 def orthogonalize(Gs: np.ndarray, steps: int = 5, coeffs=(3.4445, -4.7750, 2.0315),
                   mode: str = "gram", restart_after: int = 2, safety: float = 1.0,
-                  eps: float = EPS) -> np.ndarray:
+                  eps: float = EPS, restarts=None) -> np.ndarray:
     """Bucket [G, R, C] -> [G, R, C], each matrix on its own (fp64 throughout).
 
     The "muon" kernel card ("How it works") stacks a shape bucket into one
@@ -167,7 +182,7 @@ def orthogonalize(Gs: np.ndarray, steps: int = 5, coeffs=(3.4445, -4.7750, 2.031
     Gs = np.asarray(Gs, dtype=np.float64)
     out = np.empty_like(Gs)
     for g in range(Gs.shape[0]):
-        out[g] = ns_matrix(Gs[g], steps, coeffs, mode, restart_after, safety, eps)
+        out[g] = ns_matrix(Gs[g], steps, coeffs, mode, restart_after, safety, eps, restarts)
     return out
 
 

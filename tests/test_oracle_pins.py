@@ -307,6 +307,57 @@ def test_shifted_gram_matches_scalar_model(restart_after):
     assert rel(got, exp) <= 1e-11
 
 
+@pytest.mark.parametrize("restarts", [[2], [3, 5], [2, 4, 6, 8], [5, 10], list(range(2, 11))])
+def test_several_restarts_are_exact(restarts):
+    """Repeating the restart (Appendix B.2: restart every few iterations to
+    reach any X_T) still changes nothing in exact arithmetic: T = 10 steps with
+    the restarts listed agree with standard NS in fp64.  Restarting at every
+    step is standard NS written through Q = Z + aI."""
+    rng = np.random.default_rng(31)
+    X = oracle.normalize(rng.standard_normal((20, 70)), 1.05)
+    coeffs = [3.4445, -4.7750, 2.0315] * 5 + [15 / 8, -10 / 8, 3 / 8] * 5
+    a = oracle.standard_ns(X, coeffs, 10)
+    b = oracle.gram_ns(X, coeffs, 10, restarts=restarts)
+    assert rel(b, a) <= 1e-11
+
+
+def test_restart_list_matches_restart_after():
+    rng = np.random.default_rng(32)
+    X = oracle.normalize(rng.standard_normal((12, 40)), 1.0)
+    for r in (1, 2, 3, 4):
+        assert np.array_equal(oracle.gram_ns(X, COEFFS_MUON, 5, r), oracle.gram_ns(X, COEFFS_MUON, 5, 0, restarts=[r + 1]))
+    with pytest.raises(ValueError):
+        oracle.gram_ns(X, COEFFS_MUON, 5, restarts=[1])
+    with pytest.raises(ValueError):
+        oracle.gram_ns(X, COEFFS_MUON, 5, restarts=[6])
+
+
+@pytest.mark.parametrize("restarts", [[3, 5], [2, 4, 6], [4, 7]])
+def test_shifted_gram_several_restarts_matches_scalar_model(restarts):
+    """The scalar model of Appendix B.2.1 (-delta at every Gram formation) with
+    several restarts: each restart sets x <- q x, r <- x^2 - delta, q <- 1."""
+    delta = 4e-4
+    T = 8
+    rng = np.random.default_rng(33)
+    X = oracle.normalize(rng.standard_normal((8, 24)) @ np.diag(np.logspace(0, -2, 24)), 1.0)
+    U, S, Vt = np.linalg.svd(X, full_matrices=False)
+    x = S.copy()
+    r = x * x - delta
+    q = np.ones_like(x)
+    a, b, c = COEFFS_CLASSIC
+    for t in range(1, T + 1):
+        if t in restarts:
+            x = q * x
+            r = x * x - delta
+            q = np.ones_like(x)
+        z = a + b * r + c * r * r
+        r = r * z * z
+        q = q * z
+    exp = (U * (q * x)[None, :]) @ Vt
+    got = oracle.gram_ns(X, COEFFS_CLASSIC, T, gram_shift=delta, restarts=restarts)
+    assert rel(got, exp) <= 1e-11
+
+
 def test_naive_gram_diverges_with_spurious_negative_eigenvalue():
     """Appendix B.1.2: with h(x) = 15/8 - 10/8 x + 3/8 x^2, a negative
     eigenvalue of R grows by more than (15/8)^2 per step and diverges; the
