@@ -92,11 +92,19 @@ typedef struct {
                              FLOP count in Section 4.1 assumes; Q, RZ and R are
                              then exactly symmetric.  0: both run as general
                              products.  Other values are an argument error. */
+  uint64_t restart_mask;  /* NSG_GRAM only.  0: restart_after decides (one
+                             restart).  Otherwise bit t-1 set restarts at the
+                             top of step t (2 <= t <= steps): X <- Q X,
+                             R <- X X^T, Q <- I, as often as the mask says
+                             (Dion3 paper, Appendix B.2: repeated restarts;
+                             B.2.1: multi-restart schedules).  Bit 0 or a bit
+                             beyond `steps` is an argument error. */
 } nsg_params_t;
 
 /* Fills *p with the defaults: steps 5, the Muon triple, NSG_GRAM,
- * restart_after 2, safety 1.05, eps 1e-7, fp16 compute, sym_updates 1.  The coefficient
- * pointer refers to static storage inside the library. */
+ * restart_after 2, safety 1.05, eps 1e-7, fp16 compute, sym_updates 1,
+ * restart_mask 0.  The coefficient pointer refers to static storage inside
+ * the library. */
 void ns_default_params(nsg_params_t *p);
 
 /* Bytes of device workspace ns_orthogonalize needs for a bucket of G

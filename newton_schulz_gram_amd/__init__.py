@@ -52,6 +52,7 @@ class Params(ctypes.Structure):
         ("eps", ctypes.c_float),
         ("compute_dtype", ctypes.c_int32),
         ("sym_updates", ctypes.c_int32),
+        ("restart_mask", ctypes.c_uint64),
     ]
 
 
@@ -128,8 +129,11 @@ def _dtype_code(dt) -> int:
 
 def make_params(steps: int = 5, coeffs: Optional[Sequence[float]] = None, mode: str = "gram",
                 restart_after: int = 2, safety: float = 1.05, eps: float = 1e-7,
-                compute_dtype="f16", sym_updates: bool = True):
-    """Build an nsg_params_t.  Returns (params, keepalive) — keep both alive."""
+                compute_dtype="f16", sym_updates: bool = True, restarts: Optional[Sequence[int]] = None):
+    """Build an nsg_params_t.  Returns (params, keepalive) — keep both alive.
+
+    `restarts` lists the steps t (2..steps) at whose top the Gram iteration
+    restarts; it overrides `restart_after` (a single restart)."""
     c = list(MUON_COEFFS if coeffs is None else coeffs)
     arr = (ctypes.c_double * len(c))(*[float(x) for x in c])
     p = Params()
@@ -142,6 +146,13 @@ def make_params(steps: int = 5, coeffs: Optional[Sequence[float]] = None, mode: 
     p.eps = float(eps)
     p.compute_dtype = _dtype_code(compute_dtype)
     p.sym_updates = 1 if sym_updates else 0
+    mask = 0
+    for t in (restarts or ()):
+        t = int(t)
+        if not 1 <= t <= 64:
+            raise ValueError("restart steps must lie in 2..steps")
+        mask |= 1 << (t - 1)
+    p.restart_mask = mask
     return p, arr
 
 
@@ -179,12 +190,14 @@ def orthogonalize(G: torch.Tensor, steps: int = 5, coeffs: Optional[Sequence[flo
                   mode: str = "gram", restart_after: int = 2, safety: float = 1.05,
                   eps: float = 1e-7, compute_dtype="f16", out_dtype=None,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  status: Optional[torch.Tensor] = None, sym_updates: bool = True) -> torch.Tensor:
+                  status: Optional[torch.Tensor] = None, sym_updates: bool = True,
+                  restarts: Optional[Sequence[int]] = None) -> torch.Tensor:
     """Orthogonalize one matrix [R, C] or a bucket [G, R, C] on its GPU.
 
     sym_updates (default) runs Q Z + a Q and R Z + a R on the symmetric kernel
     (Gram mode; half the tiles, exactly symmetric results); False runs them
-    as general products.
+    as general products.  `restarts` lists several restart steps (see
+    make_params).
 
     Returns `out` (allocated if not given) with dtype out_dtype (default: the
     input's).  `status`, if given, is an int32 CUDA tensor of G entries set to
@@ -208,7 +221,8 @@ def orthogonalize(G: torch.Tensor, steps: int = 5, coeffs: Optional[Sequence[flo
         if not out.is_contiguous() or out.device != Gs.device:
             raise ValueError("out must be contiguous on the input's device")
         odt = out.dtype
-    p, _keep = make_params(steps, coeffs, mode, restart_after, safety, eps, compute_dtype, sym_updates)
+    p, _keep = make_params(steps, coeffs, mode, restart_after, safety, eps, compute_dtype, sym_updates,
+                           restarts)
     need = ctypes.c_size_t(0)
     _check(lib().ns_workspace_size(nb, R, C, ctypes.byref(p), ctypes.byref(need)), "ns_workspace_size")
     if workspace is None or workspace.numel() < need.value:

@@ -57,7 +57,9 @@ struct Plan {
   int64_t R = 0, C = 0, n = 0, m = 0, np = 0, mp = 0;
   bool tr = false;
   bool gram = false;
-  int T = 0, restart = 0;  // restart at the top of step `restart` (0: none)
+  int T = 0;
+  uint64_t restarts = 0;  // bit t-1: restart at the top of step t
+  bool restart_at(int t) const { return t >= 1 && t <= 64 && ((restarts >> (t - 1)) & 1u); }
   int cdtype = NSG_F16;
   int cfg = kTile128;
   int fexp = 0;
@@ -85,6 +87,10 @@ nsg_status_t validate_params(const nsg_params_t *p) {
   if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return NSG_ERR_INVALID_ARG;
   if (!valid_dtype(p->compute_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
   if (p->sym_updates != 0 && p->sym_updates != 1) return NSG_ERR_INVALID_ARG;
+  if (p->restart_mask != 0) {
+    if (p->restart_mask & 1u) return NSG_ERR_INVALID_ARG;  // no restart before step 1
+    if (p->steps < 64 && (p->restart_mask >> p->steps) != 0) return NSG_ERR_INVALID_ARG;
+  }
   return NSG_OK;
 }
 
@@ -155,7 +161,11 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
   P.T = p->steps;
   P.cdtype = p->compute_dtype;
   P.gram = (p->mode == NSG_GRAM) && (P.n < P.m);
-  P.restart = (P.gram && p->restart_after >= 1 && p->restart_after < P.T) ? p->restart_after + 1 : 0;
+  P.restarts = 0;
+  if (P.gram) {
+    if (p->restart_mask != 0) P.restarts = p->restart_mask;
+    else if (p->restart_after >= 1 && p->restart_after < P.T) P.restarts = 1ull << p->restart_after;
+  }
   P.cfg = choose_cfg(P.np, P.mp, P.cdtype);
   // power-of-two range shift f ~ log2(sqrt(n)): keeps X0 = X/||X||_F and
   // R0 = X0 X0^T away from fp16 subnormals (X0 entries ~ 1/sqrt(nm)).
@@ -233,12 +243,14 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
              false);
     for (int t = 1; t <= P.T; ++t) {
       const double a = P.a[t - 1], b = P.b[t - 1], c = P.c[t - 1];
-      if (t == P.restart) {
-        // X <- Q X ; R <- X X^T ; Q <- I   (Alg. 3, "restart to stabilize")
-        add_gemm(P, false, t, "X=QX", Qcur, XbT, kNone, kX1, kX1T, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
+      if (P.restart_at(t)) {
+        // X <- Q X ; R <- X X^T ; Q <- I   (Alg. 3, "restart to stabilize");
+        // repeated restarts alternate between the two X buffers
+        const int Xn = (Xb == kX1) ? kX0 : kX1, XnT = (Xb == kX1) ? kX0T : kX1T;
+        add_gemm(P, false, t, "X=QX", Qcur, XbT, kNone, Xn, XnT, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
                  xpow, false);
-        Xb = kX1; XbT = kX1T; xs = 1.0; xpow = 0;
-        add_gemm(P, true, t, "R=XXt", kX1, kX1, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
+        Xb = Xn; XbT = XnT; xs = 1.0; xpow = 0;
+        add_gemm(P, true, t, "R=XXt", Xb, Xb, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
                  0, false);
         r_scaled = false;
         Qcur = kNone;
@@ -259,7 +271,7 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
                  false);
         Qcur = qn;
       }
-      const bool need_r = (t < P.T) && (t + 1 != P.restart);
+      const bool need_r = (t < P.T) && !P.restart_at(t + 1);
       if (need_r) {
         // RZ = R Z + a R (stored with R's scale); as a general product it is
         // also written transposed, as a symmetric one RZ^T = RZ exactly
@@ -343,6 +355,7 @@ void ns_default_params(nsg_params_t *p) {
   p->eps = 1e-7f;
   p->compute_dtype = NSG_F16;
   p->sym_updates = 1;
+  p->restart_mask = 0;
 }
 
 const char *ns_status_string(nsg_status_t s) {
@@ -393,7 +406,9 @@ nsg_status_t ns_flops(int64_t R, int64_t C, const nsg_params_t *p, double *credi
     cr = 2.0 * T * (2.0 * m * n * n + n * n * n);  // 2T(2 alpha + 1) n^3
   } else {
     cr = 4.0 * T * n * n * n + 3.0 * m * n * n - 3.0 * n * n * n;  // (4T + 3 alpha - 3) n^3
-    if (P.restart) cr += 3.0 * (m * n * n - n * n * n);            // + 3(alpha - 1) n^3
+    int nr = 0;
+    for (int t = 2; t <= P.T; ++t) nr += P.restart_at(t) ? 1 : 0;
+    cr += 3.0 * nr * (m * n * n - n * n * n);  // + 3(alpha - 1) n^3 per restart
   }
   double ex = 0.0;
   for (const Launch &L : P.launches) ex += L.flops;

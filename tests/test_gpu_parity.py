@@ -284,3 +284,21 @@ def test_general_updates_moe_and_llama7b_sampled():
     print("7b general updates matrix 0: rel %.3e cos %.6f" % (rel[0], cos[0]))
     one = run(x[7:8], safety=w.safety, sym_updates=False)
     assert torch.equal(one[0], out[7])
+
+
+# ---------------------------------------------------------------------------
+# Several restarts (restart_mask) and per-step coefficient schedules
+# ---------------------------------------------------------------------------
+
+MIXED10 = [3.4445, -4.7750, 2.0315] * 5 + [15 / 8, -10 / 8, 3 / 8] * 5
+
+
+@pytest.mark.parametrize("steps,restarts", [(8, [3, 5]), (10, [2, 4, 6, 8]), (10, [5]), (6, [2, 3, 4, 5, 6])])
+def test_several_restarts(steps, restarts):
+    coeffs = (MIXED10[:15] + MIXED10[-3 * (steps - 5):]) if steps > 5 else MIXED10[:3 * steps]
+    x = custom(3, 256, 1024, "f16", "gaussian", seed=41)
+    ref = oracle.orthogonalize(x.double().numpy(), steps, coeffs, "gram", 0, 1.05, restarts=restarts)
+    out = run(x, steps=steps, coeffs=coeffs, restarts=restarts)
+    check(out, ref, "f16", f"restarts {restarts}")
+    out32 = run(x, steps=steps, coeffs=coeffs, restarts=restarts, compute_dtype="f32", out_dtype=torch.float32)
+    check(out32, ref, "f32", f"restarts {restarts} fp32")

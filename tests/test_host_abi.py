@@ -181,3 +181,31 @@ def test_sym_updates_plan():
     assert w0 - w1 >= 4096 * 4096 * 2
     # standard mode ignores it
     assert [e["kernel"] for e in nsg.plan(4096, 4096)] == [e["kernel"] for e in nsg.plan(4096, 4096, sym_updates=False)]
+
+
+def test_restart_mask_validation_and_plan():
+    p, keep = nsg.make_params(steps=6)
+    out = ctypes.c_size_t(0)
+    for mask, code in ((1, 1), (1 << 6, 1), (1 << 5, 0), (0b101010, 0)):
+        p.restart_mask = mask
+        assert nsg.lib().ns_workspace_size(1, 64, 128, ctypes.byref(p), ctypes.byref(out)) == code, mask
+    with pytest.raises(ValueError):
+        nsg.make_params(restarts=[0])
+    P = nsg.plan(768, 3072, steps=10, restarts=[3, 6, 9])
+    steps = {}
+    for e in P:
+        steps.setdefault(e["step"], []).append(e["label"])
+    for t in (3, 6, 9):
+        assert steps[t][:2] == ["X=QX", "R=XXt"] and steps[t][2] == "Z (+Q=Z+aI)"
+        assert "R=Z.RZ+aRZ" not in steps[t - 1]  # R before a restart is not needed
+    assert sum(lbl == "X=QX" for lbl in (e["label"] for e in P)) == 3
+
+
+@pytest.mark.parametrize("T,restarts", [(5, [3]), (8, [3, 5]), (10, [2, 4, 6, 8])])
+def test_credited_flops_several_restarts(T, restarts):
+    """(4T + 3 alpha - 3) n^3 plus 3 (alpha - 1) n^3 per restart (Dion3 paper,
+    Section 4.2: each restart costs 3 (alpha - 1) n^3)."""
+    n, m = 768, 3072
+    cr, _ = nsg.flops(n, m, steps=T, restarts=restarts)
+    a = m / n
+    assert cr == pytest.approx((4 * T + 3 * a - 3 + 3 * len(restarts) * (a - 1)) * n ** 3)
