@@ -18,3 +18,10 @@ from .ns_oracle import (  # noqa: F401
     flops_gram_naive,
     flops_gram_stable,
 )
+from .select_oracle import (  # noqa: F401
+    n_selected,
+    select_dim,
+    l1_norms,
+    select,
+    select_orthogonalize,
+)
