@@ -205,6 +205,56 @@ nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch,
                          void *out, int64_t ldo, void *out_t, int64_t ldt,
                          void *out_d, float diag, int32_t tile, void *stream);
 
+/* ---- Dion3 selection front-end --------------------------------------------
+ * Dion3 paper, Section 6 ("Selection", "Orthogonalization") and Algorithm 4,
+ * steps 3-4: for every matrix M of the bucket, S = the k rows (or columns)
+ * with the largest l1 norm, O = Newton-Schulz(M[S, :]) (or M[:, S]).  The
+ * update and error-feedback steps of Algorithm 4 are not part of it. */
+#define NSG_SELECT_ROWS 0
+#define NSG_SELECT_COLS 1
+#define NSG_SELECT_SMALLER (-1) /* rows if R <= C, else columns (the pages'
+                                   choice when the weight is not sharded) */
+
+/* Bytes of device workspace ns_orthogonalize_selected needs (host only).
+ * Same argument rules as ns_orthogonalize_selected. */
+nsg_status_t ns_select_workspace_size(int64_t G, int64_t R, int64_t C, int64_t k,
+                                      int32_t dim, int32_t in_dtype, int32_t out_dtype,
+                                      const nsg_params_t *p, size_t *bytes);
+
+/* Selection + orthogonalization of a bucket.
+ *   in   [G, R, C] row-major, contiguous, in_dtype (device)
+ *   out  [G, R, C] out_dtype (device; may alias in): O in the selected rows
+ *        (columns), zeros in the others
+ *   k    lines to select per matrix, 1 <= k <= n, with n = R for rows and
+ *        n = C for columns (the pages: k = ceil(f n) for a fraction f)
+ *   dim  NSG_SELECT_ROWS, NSG_SELECT_COLS or NSG_SELECT_SMALLER
+ *   idx  device [G][k] int32 or NULL: the selected indices, ascending
+ *   status  as for ns_orthogonalize (per matrix, may be NULL)
+ * Norms are fp64 sums of |M_ij| in a fixed order; equal norms go to the lower
+ * index.  O is exactly what ns_orthogonalize returns for the gathered k x C
+ * (R x k) submatrix with *p.  Errors as for ns_orthogonalize; k out of range
+ * or a bad dim is NSG_ERR_INVALID_ARG.  An empty bucket (G = 0) is a no-op. */
+nsg_status_t ns_orthogonalize_selected(const void *in, int32_t in_dtype, void *out,
+                                       int32_t out_dtype, int64_t G, int64_t R, int64_t C,
+                                       int64_t k, int32_t dim, const nsg_params_t *p,
+                                       void *workspace, size_t workspace_bytes,
+                                       int32_t *idx, int32_t *status, void *stream);
+
+/* Building blocks of the selection, exposed for tests.
+ * nsg_l1_norms: keys[g][i] = sum_j |M_g[i, j]| (dim 0) or sum_j |M_g[j, i]|
+ * (dim 1) in fp64, fixed order; keys is device [G][n].  Column norms need
+ * nsg_l1_workspace_size bytes of device workspace (0 for rows).
+ * nsg_topk: per matrix the k largest of keys[g][0..n) (equal keys: lower
+ * index first), written ascending to idx[g][0..k); pos[g][i] = rank of i
+ * among them, -1 if not selected (pos may not be NULL). */
+nsg_status_t nsg_l1_workspace_size(int64_t G, int64_t R, int64_t C, int32_t dim,
+                                   size_t *bytes);
+nsg_status_t nsg_l1_norms(const void *in, int32_t dtype, int64_t G, int64_t R, int64_t C,
+                          int32_t dim, double *keys, void *workspace,
+                          size_t workspace_bytes, void *stream);
+nsg_status_t nsg_topk(const double *keys, int64_t G, int64_t n, int64_t k, int32_t *idx,
+                      int32_t *pos, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ CPU fallback.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Sequence
 
@@ -71,7 +72,9 @@ class LaunchInfo(ctypes.Structure):
 
 EXPORTS = ("ns_default_params", "ns_workspace_size", "ns_orthogonalize", "ns_status_string",
            "ns_flops", "ns_plan", "ns_timing_enable", "ns_timing_collect", "nsg_copy",
-           "nsg_gemm_nt")
+           "nsg_gemm_nt", "ns_select_workspace_size", "ns_orthogonalize_selected",
+           "nsg_l1_workspace_size", "nsg_l1_norms", "nsg_topk")
+SELECT_ROWS, SELECT_COLS, SELECT_SMALLER = 0, 1, -1
 
 _lib = None
 
@@ -108,6 +111,16 @@ def lib() -> ctypes.CDLL:
     L.nsg_gemm_nt.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp, i64, f32, f32, vp, i64,
                               vp, i64, vp, i64, vp, f32, i32, vp]
     L.nsg_gemm_nt.restype = i32
+    L.ns_select_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32, i32, P, ctypes.POINTER(sz)]
+    L.ns_select_workspace_size.restype = i32
+    L.ns_orthogonalize_selected.argtypes = [vp, i32, vp, i32, i64, i64, i64, i64, i32, P, vp, sz, vp, vp, vp]
+    L.ns_orthogonalize_selected.restype = i32
+    L.nsg_l1_workspace_size.argtypes = [i64, i64, i64, i32, ctypes.POINTER(sz)]
+    L.nsg_l1_workspace_size.restype = i32
+    L.nsg_l1_norms.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, sz, vp]
+    L.nsg_l1_norms.restype = i32
+    L.nsg_topk.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    L.nsg_topk.restype = i32
     _lib = L
     return L
 
@@ -287,3 +300,90 @@ def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 
                                  ctypes.c_void_p(_stream_handle(A.device)))
     _check(code, "nsg_gemm_nt")
     return out, out_t, out_d
+
+
+# ---------------------------------------------------------------------------
+# Dion3 selection front-end (Dion3 paper, Section 6; Algorithm 4, steps 3-4)
+# ---------------------------------------------------------------------------
+
+def select_count(n: int, fraction: float) -> int:
+    """k = ceil(f n) lines out of n (at least 1)."""
+    if not 0.0 < fraction <= 1.0:
+        raise ValueError("fraction must lie in (0, 1]")
+    return min(n, max(1, math.ceil(fraction * n))) if n else 0
+
+
+def _select_dim(R: int, C: int, dim: int) -> int:
+    return dim if dim in (SELECT_ROWS, SELECT_COLS) else (SELECT_COLS if C < R else SELECT_ROWS)
+
+
+def orthogonalize_selected(M: torch.Tensor, fraction: float = 0.25, k: Optional[int] = None, dim: int = -1,
+                           steps: int = 5, coeffs: Optional[Sequence[float]] = None, mode: str = "gram",
+                           restart_after: int = 2, safety: float = 1.05, eps: float = 1e-7,
+                           compute_dtype="f16", out_dtype=None, out: Optional[torch.Tensor] = None,
+                           status: Optional[torch.Tensor] = None, sym_updates: bool = True,
+                           restarts: Optional[Sequence[int]] = None):
+    """Select the k = ceil(f n) rows (dim 0) or columns (dim 1; -1: the smaller
+    dimension) of largest l1 norm of every matrix, orthogonalize them, and
+    return (out, idx): out [G, R, C] holds the result in the selected lines and
+    zeros elsewhere, idx [G, k] int32 the selected indices (ascending)."""
+    if not M.is_cuda:
+        raise ValueError("orthogonalize_selected needs a GPU tensor (no CPU path)")
+    squeeze = M.dim() == 2
+    Ms = M.unsqueeze(0) if squeeze else M
+    if Ms.dim() != 3 or not Ms.is_contiguous():
+        raise ValueError("expected a contiguous [R, C] or [G, R, C] tensor")
+    G, R, C = Ms.shape
+    d = _select_dim(R, C, dim)
+    n = R if d == SELECT_ROWS else C
+    kk = select_count(n, fraction) if k is None else int(k)
+    odt = Ms.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((G, R, C), dtype=odt, device=Ms.device)
+    odt = out.dtype
+    idx = torch.empty((G, kk), dtype=torch.int32, device=Ms.device)
+    p, _keep = make_params(steps, coeffs, mode, restart_after, safety, eps, compute_dtype, sym_updates, restarts)
+    need = ctypes.c_size_t(0)
+    _check(lib().ns_select_workspace_size(G, R, C, kk, d, _dtype_code(Ms.dtype), _dtype_code(odt), ctypes.byref(p),
+                                          ctypes.byref(need)), "ns_select_workspace_size")
+    ws = torch.empty(max(1, need.value), dtype=torch.uint8, device=Ms.device)
+    with torch.cuda.device(Ms.device):
+        _check(lib().ns_orthogonalize_selected(
+            ctypes.c_void_p(Ms.data_ptr()), _dtype_code(Ms.dtype), ctypes.c_void_p(out.data_ptr()), _dtype_code(odt),
+            G, R, C, kk, d, ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), need.value,
+            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(status.data_ptr()) if status is not None else None,
+            ctypes.c_void_p(_stream_handle(Ms.device))), "ns_orthogonalize_selected")
+    if squeeze:
+        return out[0], idx[0]
+    return out, idx
+
+
+def l1_norms(M: torch.Tensor, dim: int = 0) -> torch.Tensor:
+    """fp64 l1 norms of the rows (dim 0) or columns (dim 1) of [G, R, C]."""
+    Ms = M.unsqueeze(0) if M.dim() == 2 else M
+    if not Ms.is_contiguous():
+        raise ValueError("input must be contiguous")
+    G, R, C = Ms.shape
+    n = R if dim == SELECT_ROWS else C
+    keys = torch.empty((G, n), dtype=torch.float64, device=Ms.device)
+    need = ctypes.c_size_t(0)
+    _check(lib().nsg_l1_workspace_size(G, R, C, dim, ctypes.byref(need)), "nsg_l1_workspace_size")
+    ws = torch.empty(max(1, need.value), dtype=torch.uint8, device=Ms.device)
+    with torch.cuda.device(Ms.device):
+        _check(lib().nsg_l1_norms(ctypes.c_void_p(Ms.data_ptr()), _dtype_code(Ms.dtype), G, R, C, dim,
+                                  ctypes.c_void_p(keys.data_ptr()), ctypes.c_void_p(ws.data_ptr()), need.value,
+                                  ctypes.c_void_p(_stream_handle(Ms.device))), "nsg_l1_norms")
+    return keys
+
+
+def topk(keys: torch.Tensor, k: int):
+    """(idx [G, k] ascending, pos [G, n]) of the k largest keys per row of keys."""
+    keys = keys.contiguous().to(torch.float64)
+    G, n = keys.shape
+    idx = torch.empty((G, k), dtype=torch.int32, device=keys.device)
+    pos = torch.empty((G, n), dtype=torch.int32, device=keys.device)
+    with torch.cuda.device(keys.device):
+        _check(lib().nsg_topk(ctypes.c_void_p(keys.data_ptr()), G, n, k, ctypes.c_void_p(idx.data_ptr()),
+                              ctypes.c_void_p(pos.data_ptr()), ctypes.c_void_p(_stream_handle(keys.device))),
+               "nsg_topk")
+    return idx, pos

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnsg.so")
 
-SOURCES = ["nsg_api.cpp", "nsg_kernels.hip"]
+SOURCES = ["nsg_api.cpp", "nsg_kernels.hip", "nsg_select.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -624,4 +624,128 @@ nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_
              : NSG_ERR_HIP;
 }
 
+
+}  // extern "C"
+
+// ---- selection front-end ------------------------------------------------------
+
+namespace {
+
+struct SelectLayout {
+  int dim = 0;
+  int64_t n = 0;              // lines to choose from
+  int64_t sub_R = 0, sub_C = 0;  // gathered submatrix
+  size_t keys = 0, part = 0, idx = 0, pos = 0, sub = 0, o = 0, inner = 0, total = 0;
+};
+
+nsg_status_t select_layout(int64_t G, int64_t R, int64_t C, int64_t k, int32_t dim, int32_t in_dtype,
+                           int32_t out_dtype, const nsg_params_t *p, SelectLayout &L) {
+  nsg_status_t st = validate_params(p);
+  if (st != NSG_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  st = validate_shape(G, R, C);
+  if (st != NSG_OK) return st;
+  if (dim != NSG_SELECT_ROWS && dim != NSG_SELECT_COLS && dim != NSG_SELECT_SMALLER) return NSG_ERR_INVALID_ARG;
+  L.dim = dim == NSG_SELECT_SMALLER ? (C < R ? 1 : 0) : dim;
+  L.n = L.dim == 0 ? R : C;
+  if (k < 0 || k > L.n || (k == 0 && L.n > 0)) return NSG_ERR_INVALID_ARG;
+  L.sub_R = L.dim == 0 ? k : R;
+  L.sub_C = L.dim == 0 ? C : k;
+  size_t inner = 0;
+  st = ns_workspace_size(G, L.sub_R, L.sub_C, p, &inner);
+  if (st != NSG_OK) return st;
+  const size_t A = NSG_WORKSPACE_ALIGN;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, A);
+    return o;
+  };
+  const size_t g = (size_t)G;
+  L.keys = take(8 * g * (size_t)L.n);
+  L.part = take(L.dim == 1 ? 8 * g * (size_t)l1_cols_chunks(R) * (size_t)C : 0);
+  L.idx = take(4 * g * (size_t)k);
+  L.pos = take(4 * g * (size_t)L.n);
+  L.sub = take(g * (size_t)L.sub_R * L.sub_C * dtype_size(in_dtype));
+  L.o = take(g * (size_t)L.sub_R * L.sub_C * dtype_size(out_dtype));
+  L.inner = take(inner);
+  L.total = off;
+  return NSG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nsg_status_t ns_select_workspace_size(int64_t G, int64_t R, int64_t C, int64_t k, int32_t dim, int32_t in_dtype,
+                                      int32_t out_dtype, const nsg_params_t *p, size_t *bytes) {
+  if (bytes == nullptr) return NSG_ERR_INVALID_ARG;
+  SelectLayout L;
+  nsg_status_t st = select_layout(G, R, C, k, dim, in_dtype, out_dtype, p, L);
+  if (st != NSG_OK) return st;
+  *bytes = (G == 0 || R == 0 || C == 0) ? 0 : L.total;
+  return NSG_OK;
+}
+
+nsg_status_t ns_orthogonalize_selected(const void *in, int32_t in_dtype, void *out, int32_t out_dtype, int64_t G,
+                                       int64_t R, int64_t C, int64_t k, int32_t dim, const nsg_params_t *p,
+                                       void *workspace, size_t workspace_bytes, int32_t *idx, int32_t *status,
+                                       void *stream) {
+  SelectLayout L;
+  nsg_status_t st = select_layout(G, R, C, k, dim, in_dtype, out_dtype, p, L);
+  if (st != NSG_OK) return st;
+  if (G == 0 || R == 0 || C == 0) return NSG_OK;
+  if (in == nullptr || out == nullptr) return NSG_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < L.total ||
+      (reinterpret_cast<uintptr_t>(workspace) % NSG_WORKSPACE_ALIGN) != 0)
+    return NSG_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *ws = reinterpret_cast<char *>(workspace);
+  double *keys = reinterpret_cast<double *>(ws + L.keys);
+  double *part = reinterpret_cast<double *>(ws + L.part);
+  int32_t *ix = idx != nullptr ? idx : reinterpret_cast<int32_t *>(ws + L.idx);
+  int32_t *pos = reinterpret_cast<int32_t *>(ws + L.pos);
+  void *sub = ws + L.sub, *O = ws + L.o;
+  if (launch_l1_norms(in, in_dtype, G, R, C, L.dim, keys, part, s) != hipSuccess) return NSG_ERR_HIP;
+  if (launch_topk(keys, G, L.n, k, ix, pos, s) != hipSuccess) return NSG_ERR_HIP;
+  if (launch_gather(in, in_dtype, G, R, C, L.dim, ix, k, sub, s) != hipSuccess) return NSG_ERR_HIP;
+  st = ns_orthogonalize(sub, in_dtype, O, out_dtype, G, L.sub_R, L.sub_C, p, ws + L.inner, workspace_bytes - L.inner,
+                        status, stream);
+  if (st != NSG_OK) return st;
+  if (launch_scatter(O, out_dtype, G, R, C, L.dim, pos, k, out, s) != hipSuccess) return NSG_ERR_HIP;
+  return NSG_OK;
+}
+
+nsg_status_t nsg_l1_workspace_size(int64_t G, int64_t R, int64_t C, int32_t dim, size_t *bytes) {
+  if (bytes == nullptr) return NSG_ERR_INVALID_ARG;
+  nsg_status_t st = validate_shape(G, R, C);
+  if (st != NSG_OK) return st;
+  if (dim != NSG_SELECT_ROWS && dim != NSG_SELECT_COLS) return NSG_ERR_INVALID_ARG;
+  *bytes = dim == NSG_SELECT_COLS ? 8 * (size_t)G * (size_t)l1_cols_chunks(R) * (size_t)C : 0;
+  return NSG_OK;
+}
+
+nsg_status_t nsg_l1_norms(const void *in, int32_t dtype, int64_t G, int64_t R, int64_t C, int32_t dim, double *keys,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  size_t need = 0;
+  nsg_status_t st = nsg_l1_workspace_size(G, R, C, dim, &need);
+  if (st != NSG_OK) return st;
+  if (!valid_dtype(dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (G == 0 || R == 0 || C == 0) return NSG_OK;
+  if (in == nullptr || keys == nullptr) return NSG_ERR_INVALID_ARG;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return NSG_ERR_WORKSPACE_TOO_SMALL;
+  return launch_l1_norms(in, dtype, G, R, C, dim, keys, reinterpret_cast<double *>(workspace),
+                         reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? NSG_OK
+             : NSG_ERR_HIP;
+}
+
+nsg_status_t nsg_topk(const double *keys, int64_t G, int64_t n, int64_t k, int32_t *idx, int32_t *pos, void *stream) {
+  if (G < 0 || G > 65535 || n < 0 || n > NSG_MAX_SIDE || k < 0 || k > n) return NSG_ERR_INVALID_ARG;
+  if (G == 0 || n == 0 || k == 0) return NSG_OK;
+  if (keys == nullptr || idx == nullptr || pos == nullptr) return NSG_ERR_INVALID_ARG;
+  return launch_topk(keys, G, n, k, idx, pos, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? NSG_OK
+                                                                                                  : NSG_ERR_HIP;
+}
+
 }  // extern "C"

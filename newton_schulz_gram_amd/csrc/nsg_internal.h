@@ -96,4 +96,15 @@ hipError_t launch_norm_reduce(const NormReduceArgs &a, hipStream_t s);
 hipError_t launch_scale(const ScaleArgs &a, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
 
+// selection front-end (nsg_select.hip)
+int64_t l1_cols_chunks(int64_t R);
+hipError_t launch_l1_norms(const void *in, int dtype, int64_t G, int64_t R, int64_t C, int dim, double *keys,
+                           double *part, hipStream_t s);
+hipError_t launch_topk(const double *keys, int64_t G, int64_t n, int64_t k, int32_t *idx, int32_t *pos,
+                       hipStream_t s);
+hipError_t launch_gather(const void *in, int dtype, int64_t G, int64_t R, int64_t C, int dim, const int32_t *idx,
+                         int64_t k, void *out, hipStream_t s);
+hipError_t launch_scatter(const void *O, int dtype, int64_t G, int64_t R, int64_t C, int dim, const int32_t *pos,
+                          int64_t k, void *out, hipStream_t s);
+
 }  // namespace nsg

@@ -209,3 +209,28 @@ def test_credited_flops_several_restarts(T, restarts):
     cr, _ = nsg.flops(n, m, steps=T, restarts=restarts)
     a = m / n
     assert cr == pytest.approx((4 * T + 3 * a - 3 + 3 * len(restarts) * (a - 1)) * n ** 3)
+
+
+def test_select_validation_and_workspace():
+    p, keep = nsg.make_params()
+    out = ctypes.c_size_t(0)
+    L = nsg.lib()
+    # k out of range, bad dim
+    assert L.ns_select_workspace_size(2, 64, 128, 0, 0, 0, 0, ctypes.byref(p), ctypes.byref(out)) == 1
+    assert L.ns_select_workspace_size(2, 64, 128, 65, 0, 0, 0, ctypes.byref(p), ctypes.byref(out)) == 1
+    assert L.ns_select_workspace_size(2, 64, 128, 10, 3, 0, 0, ctypes.byref(p), ctypes.byref(out)) == 1
+    assert L.ns_select_workspace_size(2, 64, 128, 10, 0, 7, 0, ctypes.byref(p), ctypes.byref(out)) == 2
+    assert L.ns_select_workspace_size(2, 64, 128, 10, 0, 0, 0, ctypes.byref(p), ctypes.byref(out)) == 0
+    rows = out.value
+    # smaller dimension of 64 x 128 is the rows: same as dim 0
+    assert L.ns_select_workspace_size(2, 64, 128, 10, -1, 0, 0, ctypes.byref(p), ctypes.byref(out)) == 0
+    assert out.value == rows
+    # columns of 256 x 100: k <= 100
+    assert L.ns_select_workspace_size(1, 256, 100, 101, -1, 0, 0, ctypes.byref(p), ctypes.byref(out)) == 1
+    assert L.ns_select_workspace_size(1, 256, 100, 25, -1, 0, 0, ctypes.byref(p), ctypes.byref(out)) == 0
+    # the inner workspace is included: at least ns_workspace_size of the submatrix
+    inner = nsg.workspace_size(2, 10, 128)
+    assert rows >= inner
+    assert L.nsg_topk(None, 1, 10, 11, None, None, None) == 1
+    assert nsg.select_count(4096, 0.25) == 1024 and nsg.select_count(10, 0.25) == 3
+    assert nsg.select_count(4096, 0.25) == oracle.n_selected(4096, 0.25)
