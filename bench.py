@@ -133,6 +133,64 @@ def cpu_baseline(w, x_cpu, budget_s: float = 30.0):
             "seconds_per_matrix": dt / done}
 
 
+def bench_select(args, w, dev):
+    """Selection front-end + Gram NS on the selected lines (Dion3 paper,
+    Algorithm 4, steps 3-4); effective FLOPs from the k x m problem."""
+    import torch
+
+    import newton_schulz_gram_amd as nsg
+    import synth
+
+    torch.cuda.set_device(dev)
+    x = synth.make(w).to(dev)
+    G, R, C = x.shape
+    dim = 1 if C < R else 0
+    n_sel = C if dim == 1 else R
+    k = nsg.select_count(n_sel, args.select_fraction)
+    kw = dict(steps=w.steps, coeffs=w.coeffs, mode=w.mode, restart_after=w.restart_after, safety=w.safety,
+              compute_dtype=w.compute, sym_updates=not args.general_updates)
+    out = torch.empty_like(x)
+    for _ in range(args.warmup):
+        nsg.orthogonalize_selected(x, args.select_fraction, dim=dim, out=out, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        nsg.orthogonalize_selected(x, args.select_fraction, dim=dim, out=out, **kw)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sub = (k, R) if dim == 1 else (k, C)   # the submatrix, short side first
+    credited, _ = nsg.flops(sub[0], sub[1], **kw) if sub[0] <= sub[1] else nsg.flops(sub[1], sub[0], **kw)
+    # the front-end alone: norms + top-k, timed on their own
+    for _ in range(2):
+        keys = nsg.l1_norms(x, dim)
+        nsg.topk(keys, k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        keys = nsg.l1_norms(x, dim)
+    torch.cuda.synchronize()
+    t_norm = (time.perf_counter() - t1) / args.steps
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        nsg.topk(keys, k)
+    torch.cuda.synchronize()
+    t_topk = (time.perf_counter() - t1) / args.steps
+    in_bytes = x.numel() * x.element_size()
+    res = {
+        "metric": f"matrices/s, Dion3 selection (f={args.select_fraction}) + Gram NS",
+        "value": round(G * args.steps / wall, 3), "unit": "matrices/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(1e3 * wall / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16" if w.compute == "f16" else w.compute,
+        "data": "synthetic",
+        "config": {"workload": w.name, "G": G, "R": R, "C": C, "select_dim": "columns" if dim else "rows",
+                   "fraction": args.select_fraction, "k": k, "submatrix": [int(v) for v in sub]},
+        "effective_tflops": round(credited * G * args.steps / wall / 1e12, 2),
+        "l1_norms": {"ms": round(1e3 * t_norm, 3), "gbs": round(in_bytes / t_norm / 1e9, 1)},
+        "topk_ms": round(1e3 * t_topk, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +198,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select-fraction", type=float, default=None,
+                    help="time the Dion3 selection front-end: k = ceil(f n) lines of the smaller dimension")
     ap.add_argument("--general-updates", action="store_true",
                     help="run Q Z + a Q and R Z + a R as general products (default: symmetric kernel)")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
@@ -163,6 +223,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.select_fraction is not None:
+        return bench_select(args, w, dev)
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     t_gen = time.perf_counter()

@@ -60,6 +60,33 @@ __global__ void __launch_bounds__(256) l1_rows_kernel(const TI *__restrict__ in,
 // ---------------------------------------------------------------------------
 constexpr int kColChunk = 512;
 
+// Vector form: a thread owns 16 bytes of consecutive columns (same per-column
+// order of rows, so the sums equal the scalar kernel's bit for bit).
+template <typename TI>
+__global__ void __launch_bounds__(256) l1_cols_partial_vec_kernel(const TI *__restrict__ in, int64_t R, int64_t C,
+                                                                  int nchunks, double *__restrict__ part) {
+  constexpr int V = 16 / (int)sizeof(TI);
+  typedef TI vec_t __attribute__((ext_vector_type(V)));
+  const int64_t col0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+  const int chunk = blockIdx.y, g = blockIdx.z;
+  if (col0 >= C) return;
+  const int64_t r0 = (int64_t)chunk * kColChunk;
+  int64_t r1 = r0 + kColChunk;
+  if (r1 > R) r1 = R;
+  const TI *src = in + (size_t)g * R * C + col0;
+  double s[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) s[v] = 0.0;
+  for (int64_t r = r0; r < r1; ++r) {
+    const vec_t x = *reinterpret_cast<const vec_t *>(src + (size_t)r * C);
+#pragma unroll
+    for (int v = 0; v < V; ++v) s[v] += absd<TI>(x[v]);
+  }
+  double *dst = part + ((size_t)g * nchunks + chunk) * C + col0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) dst[v] = s[v];
+}
+
 template <typename TI>
 __global__ void __launch_bounds__(256) l1_cols_partial_kernel(const TI *__restrict__ in, int64_t R, int64_t C,
                                                               int nchunks, double *__restrict__ part) {
@@ -226,6 +253,27 @@ __global__ void __launch_bounds__(256) scatter_rows_kernel(const T *__restrict__
 }
 
 template <typename T>
+__global__ void __launch_bounds__(256) scatter_cols_vec_kernel(const T *__restrict__ O, int64_t R, int64_t C,
+                                                               const int32_t *__restrict__ pos, int64_t k,
+                                                               T *__restrict__ out) {
+  constexpr int V = 16 / (int)sizeof(T);
+  typedef T vec_t __attribute__((ext_vector_type(V)));
+  const int64_t c0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * V;
+  const int64_t r = blockIdx.x;
+  const int g = blockIdx.z;
+  if (c0 >= C) return;
+  const int32_t *pg = pos + (size_t)g * C + c0;
+  const T *orow = O + ((size_t)g * R + r) * k;
+  vec_t w;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int p = pg[v];
+    w[v] = p < 0 ? (T)0.f : orow[p];
+  }
+  *reinterpret_cast<vec_t *>(out + ((size_t)g * R + r) * C + c0) = w;
+}
+
+template <typename T>
 __global__ void __launch_bounds__(256) scatter_cols_kernel(const T *__restrict__ O, int64_t R, int64_t C,
                                                            const int32_t *__restrict__ pos, int64_t k,
                                                            T *__restrict__ out) {
@@ -260,12 +308,20 @@ hipError_t launch_l1_norms(const void *in, int dtype, int64_t G, int64_t R, int6
 #undef NSG_L1R
   } else {
     const int nch = (int)l1_cols_chunks(R);
+    const size_t es = dtype == NSG_F32 ? 4 : 2;
+    const int64_t V = 16 / (int64_t)es;
+    const bool vec = (reinterpret_cast<uintptr_t>(in) % 16 == 0) && (C % V) == 0;
     dim3 grid((unsigned)((C + 255) / 256), (unsigned)nch, (unsigned)G);
+    dim3 gridv((unsigned)((C / V + 255) / 256), (unsigned)nch, (unsigned)G);
+#define NSG_L1C(TI)                                                                                              \
+  if (vec) hipLaunchKernelGGL(l1_cols_partial_vec_kernel<TI>, gridv, dim3(256), 0, s, (const TI *)in, R, C, nch, part); \
+  else hipLaunchKernelGGL(l1_cols_partial_kernel<TI>, grid, dim3(256), 0, s, (const TI *)in, R, C, nch, part)
     switch (dtype) {
-      case NSG_F16: hipLaunchKernelGGL(l1_cols_partial_kernel<_Float16>, grid, dim3(256), 0, s, (const _Float16 *)in, R, C, nch, part); break;
-      case NSG_BF16: hipLaunchKernelGGL(l1_cols_partial_kernel<__bf16>, grid, dim3(256), 0, s, (const __bf16 *)in, R, C, nch, part); break;
-      default: hipLaunchKernelGGL(l1_cols_partial_kernel<float>, grid, dim3(256), 0, s, (const float *)in, R, C, nch, part); break;
+      case NSG_F16: NSG_L1C(_Float16); break;
+      case NSG_BF16: NSG_L1C(__bf16); break;
+      default: NSG_L1C(float); break;
     }
+#undef NSG_L1C
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(l1_cols_combine_kernel, dim3((unsigned)((C + 255) / 256), (unsigned)G), dim3(256), 0, s,
@@ -299,9 +355,15 @@ static hipError_t scatter_t(const void *O, int64_t G, int64_t R, int64_t C, int 
   if (dim == 0)
     hipLaunchKernelGGL(scatter_rows_kernel<T>, dim3((unsigned)R, (unsigned)G), dim3(256), 0, s, (const T *)O, R, C,
                        pos, k, (T *)out);
-  else
-    hipLaunchKernelGGL(scatter_cols_kernel<T>, dim3((unsigned)R, (unsigned)((C + 255) / 256), (unsigned)G),
-                       dim3(256), 0, s, (const T *)O, R, C, pos, k, (T *)out);
+  else {
+    constexpr int64_t V = 16 / (int64_t)sizeof(T);
+    if ((reinterpret_cast<uintptr_t>(out) % 16 == 0) && (C % V) == 0)
+      hipLaunchKernelGGL(scatter_cols_vec_kernel<T>, dim3((unsigned)R, (unsigned)((C / V + 255) / 256), (unsigned)G),
+                         dim3(256), 0, s, (const T *)O, R, C, pos, k, (T *)out);
+    else
+      hipLaunchKernelGGL(scatter_cols_kernel<T>, dim3((unsigned)R, (unsigned)((C + 255) / 256), (unsigned)G),
+                         dim3(256), 0, s, (const T *)O, R, C, pos, k, (T *)out);
+  }
   return hipGetLastError();
 }
 
