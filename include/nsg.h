@@ -255,6 +255,43 @@ nsg_status_t nsg_l1_norms(const void *in, int32_t dtype, int64_t G, int64_t R, i
 nsg_status_t nsg_topk(const double *keys, int64_t G, int64_t n, int64_t k, int32_t *idx,
                       int32_t *pos, void *stream);
 
+/* ---- The Muon step around the orthogonalization -------------------------
+ * Dion3 paper, Section 2.1, Eq. (1): M <- mu M + G, W <- W - lr polar(M);
+ * Algorithm 4, steps 8-9: decoupled weight decay and the update in one
+ * pass, W <- (1 - lr wd) W - lr s O; the "muon" kernel card: bf16 W written
+ * back with counter-based stochastic rounding keyed by the element's global
+ * index.  All arithmetic is fp32, one rounding per operation, no fused
+ * multiply-add: t = mu m, m' = t + g; c1 = f32(1 - lr wd), c2 = f32(lr s)
+ * (from the double arguments), w' = c1 w - c2 o.  Stochastic rounding adds
+ * 16 random bits to the fp32 pattern and truncates (non-finite values round
+ * to nearest even); the bits come from Philox-4x32-10 (Salmon et al., SC 2011)
+ * with key = seed and counter = (i >> 3, step): element i uses the 16-bit half
+ * i & 1 of output word (i & 7) >> 1.  Reproducible bit for bit for a fixed
+ * (seed, step). */
+
+/* M [n] (F32 or BF16, rounded to nearest even) <- mu M + G [n] (any dtype).
+ * Device pointers; returns before running (stream order). */
+nsg_status_t ns_muon_momentum(void *M, int32_t m_dtype, const void *G, int32_t g_dtype,
+                              int64_t n, float mu, void *stream);
+
+/* W [n] (F32, or BF16 with stochastic != 0 for stochastic rounding, else
+ * nearest even) <- (1 - lr wd) W - lr scale O [n] (any dtype). */
+nsg_status_t ns_muon_update(void *W, int32_t w_dtype, const void *O, int32_t o_dtype, int64_t n,
+                            double lr, double weight_decay, double scale, int32_t stochastic,
+                            uint64_t seed, uint64_t step, void *stream);
+
+/* One Muon step for a bucket of G matrices R x C: ns_muon_momentum, then
+ * O = ns_orthogonalize(M) with *p (fp32 output in the workspace), then
+ * ns_muon_update(W, O).  W, M, Gr are [G, R, C] contiguous device arrays;
+ * status as for ns_orthogonalize.  Workspace: ns_muon_workspace_size. */
+nsg_status_t ns_muon_workspace_size(int64_t G, int64_t R, int64_t C, const nsg_params_t *p,
+                                    size_t *bytes);
+nsg_status_t ns_muon_step(void *W, int32_t w_dtype, void *M, int32_t m_dtype, const void *Gr,
+                          int32_t g_dtype, int64_t G, int64_t R, int64_t C, float mu, double lr,
+                          double weight_decay, double scale, int32_t stochastic, uint64_t seed,
+                          uint64_t step, const nsg_params_t *p, void *workspace,
+                          size_t workspace_bytes, int32_t *status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -73,7 +73,8 @@ class LaunchInfo(ctypes.Structure):
 EXPORTS = ("ns_default_params", "ns_workspace_size", "ns_orthogonalize", "ns_status_string",
            "ns_flops", "ns_plan", "ns_timing_enable", "ns_timing_collect", "nsg_copy",
            "nsg_gemm_nt", "ns_select_workspace_size", "ns_orthogonalize_selected",
-           "nsg_l1_workspace_size", "nsg_l1_norms", "nsg_topk")
+           "nsg_l1_workspace_size", "nsg_l1_norms", "nsg_topk", "ns_muon_momentum", "ns_muon_update",
+           "ns_muon_workspace_size", "ns_muon_step")
 SELECT_ROWS, SELECT_COLS, SELECT_SMALLER = 0, 1, -1
 
 _lib = None
@@ -121,6 +122,16 @@ def lib() -> ctypes.CDLL:
     L.nsg_l1_norms.restype = i32
     L.nsg_topk.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     L.nsg_topk.restype = i32
+    f64, u64 = ctypes.c_double, ctypes.c_uint64
+    L.ns_muon_momentum.argtypes = [vp, i32, vp, i32, i64, f32, vp]
+    L.ns_muon_momentum.restype = i32
+    L.ns_muon_update.argtypes = [vp, i32, vp, i32, i64, f64, f64, f64, i32, u64, u64, vp]
+    L.ns_muon_update.restype = i32
+    L.ns_muon_workspace_size.argtypes = [i64, i64, i64, P, ctypes.POINTER(sz)]
+    L.ns_muon_workspace_size.restype = i32
+    L.ns_muon_step.argtypes = [vp, i32, vp, i32, vp, i32, i64, i64, i64, f32, f64, f64, f64, i32, u64, u64, P,
+                               vp, sz, vp, vp]
+    L.ns_muon_step.restype = i32
     _lib = L
     return L
 
@@ -387,3 +398,59 @@ def topk(keys: torch.Tensor, k: int):
                               ctypes.c_void_p(pos.data_ptr()), ctypes.c_void_p(_stream_handle(keys.device))),
                "nsg_topk")
     return idx, pos
+
+
+# ---------------------------------------------------------------------------
+# The Muon step (Dion3 paper, Eq. (1); Algorithm 4, steps 8-9; muon card)
+# ---------------------------------------------------------------------------
+
+def muon_momentum(M: torch.Tensor, G: torch.Tensor, mu: float):
+    """In place: M <- mu M + G (fp32 arithmetic; M is float32 or bfloat16)."""
+    if M.numel() != G.numel() or not (M.is_contiguous() and G.is_contiguous()):
+        raise ValueError("M and G must be contiguous with the same number of elements")
+    with torch.cuda.device(M.device):
+        _check(lib().ns_muon_momentum(ctypes.c_void_p(M.data_ptr()), _dtype_code(M.dtype), ctypes.c_void_p(G.data_ptr()),
+                                      _dtype_code(G.dtype), M.numel(), float(mu),
+                                      ctypes.c_void_p(_stream_handle(M.device))), "ns_muon_momentum")
+    return M
+
+
+def muon_update(W: torch.Tensor, O: torch.Tensor, lr: float, weight_decay: float = 0.0, scale: float = 1.0,
+                stochastic: bool = True, seed: int = 0, step: int = 0):
+    """In place: W <- (1 - lr wd) W - lr scale O; a bf16 W is written back with
+    counter-based stochastic rounding (seed, step, element index)."""
+    if W.numel() != O.numel() or not (W.is_contiguous() and O.is_contiguous()):
+        raise ValueError("W and O must be contiguous with the same number of elements")
+    with torch.cuda.device(W.device):
+        _check(lib().ns_muon_update(ctypes.c_void_p(W.data_ptr()), _dtype_code(W.dtype), ctypes.c_void_p(O.data_ptr()),
+                                    _dtype_code(O.dtype), W.numel(), float(lr), float(weight_decay), float(scale),
+                                    1 if stochastic else 0, int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1),
+                                    ctypes.c_void_p(_stream_handle(W.device))), "ns_muon_update")
+    return W
+
+
+def muon_step(W: torch.Tensor, M: torch.Tensor, G: torch.Tensor, mu: float, lr: float, weight_decay: float = 0.0,
+              scale: float = 1.0, stochastic: bool = True, seed: int = 0, step: int = 0,
+              status: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, **kw):
+    """One Muon step for a bucket [G, R, C] (or one [R, C] matrix), in place on
+    W and M; keyword arguments set the Newton-Schulz parameters."""
+    Ws, Ms, Gs = (t.unsqueeze(0) if t.dim() == 2 else t for t in (W, M, G))
+    if not (Ws.shape == Ms.shape == Gs.shape) or Ws.dim() != 3:
+        raise ValueError("W, M and G must share a [G, R, C] or [R, C] shape")
+    if not (Ws.is_contiguous() and Ms.is_contiguous() and Gs.is_contiguous()):
+        raise ValueError("W, M and G must be contiguous")
+    nb, R, C = Ws.shape
+    p, _keep = make_params(**kw)
+    need = ctypes.c_size_t(0)
+    _check(lib().ns_muon_workspace_size(nb, R, C, ctypes.byref(p), ctypes.byref(need)), "ns_muon_workspace_size")
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(1, need.value), dtype=torch.uint8, device=Ws.device)
+    with torch.cuda.device(Ws.device):
+        _check(lib().ns_muon_step(
+            ctypes.c_void_p(Ws.data_ptr()), _dtype_code(Ws.dtype), ctypes.c_void_p(Ms.data_ptr()), _dtype_code(Ms.dtype),
+            ctypes.c_void_p(Gs.data_ptr()), _dtype_code(Gs.dtype), nb, R, C, float(mu), float(lr), float(weight_decay),
+            float(scale), 1 if stochastic else 0, int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1), ctypes.byref(p),
+            ctypes.c_void_p(workspace.data_ptr()), need.value,
+            ctypes.c_void_p(status.data_ptr()) if status is not None else None,
+            ctypes.c_void_p(_stream_handle(Ws.device))), "ns_muon_step")
+    return W, M

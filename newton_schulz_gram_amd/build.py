@@ -18,7 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnsg.so")
 
-SOURCES = ["nsg_api.cpp", "nsg_kernels.hip", "nsg_select.hip"]
+SOURCES = ["nsg_api.cpp", "nsg_kernels.hip", "nsg_select.hip", "nsg_muon.hip"]
+# per-source flags: the Muon-step kernels round every fp32 operation on its own
+# (hipcc's default contraction would fuse multiply-adds and ignore pragmas)
+EXTRA = {"nsg_muon.hip": ["-ffp-contract=off"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -36,7 +39,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        cmd = [HIPCC, *common, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *common, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"

@@ -748,4 +748,68 @@ nsg_status_t nsg_topk(const double *keys, int64_t G, int64_t n, int64_t k, int32
                                                                                                   : NSG_ERR_HIP;
 }
 
+
+// ---- Muon step ------------------------------------------------------------------
+
+nsg_status_t ns_muon_momentum(void *M, int32_t m_dtype, const void *G, int32_t g_dtype, int64_t n, float mu,
+                              void *stream) {
+  if (m_dtype != NSG_F32 && m_dtype != NSG_BF16) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (!valid_dtype(g_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (n < 0 || !std::isfinite(mu)) return NSG_ERR_INVALID_ARG;
+  if (n == 0) return NSG_OK;
+  if (M == nullptr || G == nullptr) return NSG_ERR_INVALID_ARG;
+  return launch_muon_momentum(M, m_dtype, G, g_dtype, n, mu, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? NSG_OK
+             : NSG_ERR_HIP;
+}
+
+nsg_status_t ns_muon_update(void *W, int32_t w_dtype, const void *O, int32_t o_dtype, int64_t n, double lr,
+                            double weight_decay, double scale, int32_t stochastic, uint64_t seed, uint64_t step,
+                            void *stream) {
+  if (w_dtype != NSG_F32 && w_dtype != NSG_BF16) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (!valid_dtype(o_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (n < 0 || !std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(scale)) return NSG_ERR_INVALID_ARG;
+  if (n == 0) return NSG_OK;
+  if (W == nullptr || O == nullptr) return NSG_ERR_INVALID_ARG;
+  const float c1 = (float)(1.0 - lr * weight_decay), c2 = (float)(lr * scale);
+  return launch_muon_update(W, w_dtype, O, o_dtype, n, c1, c2, stochastic ? 1 : 0, seed, step,
+                            reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? NSG_OK
+             : NSG_ERR_HIP;
+}
+
+nsg_status_t ns_muon_workspace_size(int64_t G, int64_t R, int64_t C, const nsg_params_t *p, size_t *bytes) {
+  if (bytes == nullptr) return NSG_ERR_INVALID_ARG;
+  size_t inner = 0;
+  nsg_status_t st = ns_workspace_size(G, R, C, p, &inner);
+  if (st != NSG_OK) return st;
+  *bytes = inner == 0 ? 0 : align_up((size_t)G * R * C * 4, NSG_WORKSPACE_ALIGN) + inner;
+  return NSG_OK;
+}
+
+nsg_status_t ns_muon_step(void *W, int32_t w_dtype, void *M, int32_t m_dtype, const void *Gr, int32_t g_dtype,
+                          int64_t G, int64_t R, int64_t C, float mu, double lr, double weight_decay, double scale,
+                          int32_t stochastic, uint64_t seed, uint64_t step, const nsg_params_t *p, void *workspace,
+                          size_t workspace_bytes, int32_t *status, void *stream) {
+  size_t need = 0;
+  nsg_status_t st = ns_muon_workspace_size(G, R, C, p, &need);
+  if (st != NSG_OK) return st;
+  if ((w_dtype != NSG_F32 && w_dtype != NSG_BF16) || (m_dtype != NSG_F32 && m_dtype != NSG_BF16) ||
+      !valid_dtype(g_dtype))
+    return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (G == 0 || R == 0 || C == 0) return NSG_OK;
+  if (W == nullptr || M == nullptr || Gr == nullptr) return NSG_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) % NSG_WORKSPACE_ALIGN) != 0)
+    return NSG_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t n = G * R * C;
+  st = ns_muon_momentum(M, m_dtype, Gr, g_dtype, n, mu, stream);
+  if (st != NSG_OK) return st;
+  char *ws = reinterpret_cast<char *>(workspace);
+  const size_t o_bytes = align_up((size_t)n * 4, NSG_WORKSPACE_ALIGN);
+  st = ns_orthogonalize(M, m_dtype, ws, NSG_F32, G, R, C, p, ws + o_bytes, workspace_bytes - o_bytes, status, stream);
+  if (st != NSG_OK) return st;
+  return ns_muon_update(W, w_dtype, ws, NSG_F32, n, lr, weight_decay, scale, stochastic, seed, step, stream);
+}
+
 }  // extern "C"

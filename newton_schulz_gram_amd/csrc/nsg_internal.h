@@ -96,6 +96,12 @@ hipError_t launch_norm_reduce(const NormReduceArgs &a, hipStream_t s);
 hipError_t launch_scale(const ScaleArgs &a, hipStream_t s);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
 
+// Muon step (nsg_muon.hip)
+hipError_t launch_muon_momentum(void *M, int m_dtype, const void *G, int g_dtype, int64_t n, float mu,
+                                hipStream_t s);
+hipError_t launch_muon_update(void *W, int w_dtype, const void *O, int o_dtype, int64_t n, float c1, float c2,
+                              int stochastic, uint64_t seed, uint64_t step, hipStream_t s);
+
 // selection front-end (nsg_select.hip)
 int64_t l1_cols_chunks(int64_t R);
 hipError_t launch_l1_norms(const void *in, int dtype, int64_t G, int64_t R, int64_t C, int dim, double *keys,
