@@ -191,6 +191,56 @@ def bench_select(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def bench_muon(args, w, dev):
+    """One Muon step per timed step (Dion3 paper, Eq. (1) with decoupled weight
+    decay; bf16 W written back with stochastic rounding, fp32 momentum)."""
+    import torch
+
+    import newton_schulz_gram_amd as nsg
+    import synth
+
+    torch.cuda.set_device(dev)
+    grad = synth.make(w).to(dev)
+    G, R, C = grad.shape
+    W = torch.randn(G, R, C, device=dev).to(torch.bfloat16)
+    M = torch.zeros(G, R, C, device=dev, dtype=torch.float32)
+    kw = dict(steps=w.steps, coeffs=w.coeffs, mode=w.mode, restart_after=w.restart_after, safety=w.safety,
+              compute_dtype=w.compute, sym_updates=not args.general_updates)
+    for i in range(args.warmup):
+        nsg.muon_step(W, M, grad, 0.95, 0.02, 0.01, 1.0, seed=1, step=i, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        nsg.muon_step(W, M, grad, 0.95, 0.02, 0.01, 1.0, seed=1, step=args.warmup + i, **kw)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the elementwise kernels on their own
+    O = torch.empty(G, R, C, device=dev, dtype=torch.float32)
+    n = W.numel()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        nsg.muon_momentum(M, grad, 0.95)
+    torch.cuda.synchronize()
+    tm = (time.perf_counter() - t1) / args.steps
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        nsg.muon_update(W, O, 0.0, 0.0, 1.0, seed=1, step=i)
+    torch.cuda.synchronize()
+    tu = (time.perf_counter() - t1) / args.steps
+    credited, _ = nsg.flops(R, C, **kw)
+    res = {
+        "metric": "matrices/s, Muon step (momentum + Gram NS + update, bf16 stochastic rounding)",
+        "value": round(G * args.steps / wall, 3), "unit": "matrices/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(1e3 * wall / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16" if w.compute == "f16" else w.compute,
+        "data": "synthetic", "config": {"workload": w.name, "G": G, "R": R, "C": C, "W": "bf16", "M": "f32"},
+        "effective_tflops": round(credited * G * args.steps / wall / 1e12, 2),
+        "momentum": {"ms": round(1e3 * tm, 3), "gbs": round(n * 10 / tm / 1e9, 1)},
+        "update": {"ms": round(1e3 * tu, 3), "gbs": round(n * 8 / tu / 1e9, 1)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +250,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--select-fraction", type=float, default=None,
                     help="time the Dion3 selection front-end: k = ceil(f n) lines of the smaller dimension")
+    ap.add_argument("--muon-step", action="store_true",
+                    help="time the whole Muon step (momentum, orthogonalization, update) on the bucket")
     ap.add_argument("--general-updates", action="store_true",
                     help="run Q Z + a Q and R Z + a R as general products (default: symmetric kernel)")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
@@ -225,6 +277,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.select_fraction is not None:
         return bench_select(args, w, dev)
+    if args.muon_step:
+        return bench_muon(args, w, dev)
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     t_gen = time.perf_counter()
