@@ -22,10 +22,6 @@
 
 #include "nsg_internal.h"
 
-#ifndef NSG_PF_AHEAD
-#define NSG_PF_AHEAD 2
-#endif
-
 namespace nsg {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -363,7 +359,7 @@ __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "me
 
 constexpr int kStages256 = 2;
 // stages between a prefetched slice and its direct load
-constexpr int kPrefetchAhead = NSG_PF_AHEAD;
+constexpr int kPrefetchAhead = 2;
 
 // 16-byte vector of 8 16-bit values, or of 4 floats.
 // Output stores of the GEMM epilogues are non-temporal: the tiles are not
