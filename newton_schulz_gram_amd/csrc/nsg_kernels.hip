@@ -25,6 +25,7 @@
 namespace nsg {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -385,11 +386,37 @@ template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_
 // Inside a diagonal tile of a symmetric product only the lower half is
 // stored, to both places, so the output is exactly symmetric.  The
 // non-finite check of out0 runs only when a status array is given.
-template <typename T, typename TO, bool SYM, int NW, int TN, int PITCH>
-__device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x16 (&acc)[4][TN], float *lds, int g,
+// Phase A writers: one wave's 128 x 128 accumulators into the column-major
+// staging area (16-byte writes of 4 consecutive rows of one column).
+// 32x32 MFMA tiles: lane l, register r = row 8 (r/4) + 4 (l/32) + r%4, column l%32.
+template <int PITCH, int TN>
+__device__ __forceinline__ void stage_acc(const f32x16 (&acc)[4][TN], float *lds, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      float *col = lds + (wn * TN * 32 + j * 32 + (lane & 31)) * PITCH + i * 32 + 4 * (lane >> 5);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4 *>(col + 8 * r4) = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                                                acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
+    }
+}
+// 16x16 MFMA tiles: lane l, register r = row 4 (l/16) + r, column l%16.
+template <int PITCH, int TN>
+__device__ __forceinline__ void stage_acc(const f32x4 (&acc)[8][TN], float *lds, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      *reinterpret_cast<float4 *>(lds + (wn * TN * 16 + j * 16 + (lane & 15)) * PITCH + i * 16 + 4 * (lane >> 4)) =
+          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+}
+
+template <typename T, typename TO, bool SYM, int NW, int PITCH, typename ACC>
+__device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                   int tm, int tn, int wm, int wn, int lane, int tid) {
   static_assert(PITCH % 4 == 0, "16-byte staging writes");
-  constexpr int WN = TN * 32;
   constexpr int VT = 16 / (int)sizeof(T);   // elements of T per 16 bytes
   constexpr int VO = 16 / (int)sizeof(TO);  // elements of TO per 16 bytes
   float sc = 1.f;
@@ -416,18 +443,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
     const int gcol0 = tn * 256;
     const bool interior = grow0 + 128 <= p.Mv && gcol0 + 256 <= p.Nv;
     // ---- A: accumulators -> LDS ----
-    if (wm == pass) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          float *col = lds + (wn * WN + j * 32 + (lane & 31)) * PITCH + i * 32 + 4 * (lane >> 5);
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            *reinterpret_cast<float4 *>(col + 8 * r4) = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
-                                                                    acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
-        }
-    }
+    if (wm == pass) stage_acc<PITCH>(acc, lds, wn, lane);
     __syncthreads();
     // ---- B1: row orientation ----
     // Fast path: the whole pass is inside the valid corner, out0 takes 16-byte
@@ -655,21 +671,59 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const f32x1
   if (chk && __ballot(!finite) != 0 && lane == 0) p.status[g] = 1;
 }
 
-template <typename T, bool SYM, int NW, int TN, int PITCH>
-__device__ __forceinline__ void staged_epilogue(const GemmArgs &p, const f32x16 (&acc)[4][TN], float *lds, int g,
+template <typename T, bool SYM, int NW, int PITCH, typename ACC>
+__device__ __forceinline__ void staged_epilogue(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                 int tm, int tn, int wm, int wn, int lane, int tid) {
   if constexpr (SYM) {
-    staged_epilogue_t<T, T, true, NW, TN, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+    staged_epilogue_t<T, T, true, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   } else {
     if (p.out0_dtype == NSG_F16)
-      staged_epilogue_t<T, _Float16, false, NW, TN, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, _Float16, false, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
     else if (p.out0_dtype == NSG_BF16)
-      staged_epilogue_t<T, __bf16, false, NW, TN, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, __bf16, false, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
     else
-      staged_epilogue_t<T, float, false, NW, TN, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, float, false, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   }
 }
 
+
+// Block id -> (matrix, tile) of the 256 x 256 kernels.  Workgroups reach the
+// XCDs round-robin (block L on XCD L % 8).  Rounds of 8 x 32 consecutive tiles
+// are split so XCD x takes chunk x (32 tiles = the workgroups it runs at once,
+// a 4 x 8 block of the grouped order below): the 8 XCDs then work on
+// neighbouring tiles of the same matrix, whose operands stay in the shared
+// last-level cache, while each XCD's 32 tiles share rows in its own L2.  The
+// tail that does not fill a round keeps the identity map.
+template <bool SYM>
+__device__ __forceinline__ void tile_256(const GemmArgs &p, int &g, int &tm, int &tn) {
+  const unsigned L = blockIdx.x, total = gridDim.x;
+  constexpr unsigned CH = 32, ROUND = 8 * CH;
+  const unsigned full = total / ROUND;
+  unsigned V = L;
+  if (L < full * ROUND) {
+    const unsigned xcd = L & 7u, slot = L >> 3;
+    V = (slot / CH) * ROUND + xcd * CH + (slot % CH);
+  }
+  const int tiles_m = p.M >> 8, tiles_n = p.N >> 8;
+  const int tiles = SYM ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
+  g = (int)(V / (unsigned)tiles);
+  const int t = (int)(V - (unsigned)g * (unsigned)tiles);
+  if constexpr (SYM) {
+    int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+    while (r * (r + 1) / 2 > t) --r;
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    tm = r;
+    tn = t - r * (r + 1) / 2;
+  } else {
+    constexpr int GM = 4;
+    const int in_group = GM * tiles_n;
+    const int first = (t / in_group) * GM;
+    const int gsz = min(tiles_m - first, GM);
+    const int w = t - (t / in_group) * in_group;
+    tm = first + w % gsz;
+    tn = w / gsz;
+  }
+}
 
 template <int DT, bool SYM, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
@@ -698,41 +752,8 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // ---- block id -> (matrix, tile) ----
-  // Workgroups reach the XCDs round-robin (block L on XCD L % 8).  Rounds of
-  // 8 x 32 consecutive tiles are split so XCD x takes chunk x (32 tiles = the
-  // workgroups it runs at once, a 4 x 8 block of the grouped order below): the
-  // 8 XCDs then work on neighbouring tiles of the same matrix, whose operands
-  // stay in the shared last-level cache, while each XCD's 32 tiles share rows
-  // in its own L2.  The tail that does not fill a round keeps the identity map.
-  const unsigned L = blockIdx.x, total = gridDim.x;
-  constexpr unsigned CH = 32, ROUND = 8 * CH;
-  const unsigned full = total / ROUND;
-  unsigned V = L;
-  if (L < full * ROUND) {
-    const unsigned xcd = L & 7u, slot = L >> 3;
-    V = (slot / CH) * ROUND + xcd * CH + (slot % CH);
-  }
-  const int tiles_m = p.M >> 8, tiles_n = p.N >> 8;
-  const int tiles = SYM ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
-  const int g = (int)(V / (unsigned)tiles);
-  const int t = (int)(V - (unsigned)g * (unsigned)tiles);
-  int tm, tn;
-  if constexpr (SYM) {
-    int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
-    while (r * (r + 1) / 2 > t) --r;
-    while ((r + 1) * (r + 2) / 2 <= t) ++r;
-    tm = r;
-    tn = t - r * (r + 1) / 2;
-  } else {
-    constexpr int GM = 4;
-    const int in_group = GM * tiles_n;
-    const int first = (t / in_group) * GM;
-    const int gsz = min(tiles_m - first, GM);
-    const int w = t - (t / in_group) * in_group;
-    tm = first + w % gsz;
-    tn = w / gsz;
-  }
+  int g, tm, tn;
+  tile_256<SYM>(p, g, tm, tn);
 
   // ---- direct-load sources: wave w fills the 1 KB blocks b = w + NW i of
   //      each slice (rows 8 b .. 8 b + 7; lane l writes chunk slot l % 8 of
@@ -863,7 +884,191 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
   // ---- fp32 epilogue (same contract as gemm_nt_kernel), staged in LDS ----
   wait_vmcnt<0>();  // the last (unused) refill has landed
   __syncthreads();  // all waves are done with the operand stages
-  staged_epilogue<T, SYM, NW, TN, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
+  staged_epilogue<T, SYM, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
+}
+
+
+// ---------------------------------------------------------------------------
+// 256x256 batched NT GEMM for fp16 / bf16 on 16x16x32 MFMAs.  Same tile,
+// operand staging, block order and epilogue as gemm256_kernel; each wave owns
+// 128 x 128 as 8 x 8 blocks of 16 x 16 (f32x4 accumulators, 256 per lane).
+// A 64-element stage is two 32-element MFMA K-steps, and each block's two
+// MFMAs of a stage are issued back to back (the second accumulates onto the
+// first's result).  At the shader clock this chip sustains under its power
+// limit this order of 16x16x32 MFMAs delivers more fp16 throughput than
+// 32x32x16 (measured on random operands: ~2.05 vs ~1.65 PFLOP/s).
+//
+// All fragments of a stage (8 A and 8 B blocks x 2 K-steps, 128 VGPRs) are
+// in registers when its MFMAs start; the next stage's fragments replace them
+// as they die: a stage runs columns 0-3 (H0) then columns 4-7 (H1), row by
+// row, so B columns 0-3 are free during H1, A row i after H1 row i, and B
+// columns 4-7 at the end.  LDS slot use per stage k (slot k % 2):
+//   H0 row 1: barrier A (every wave read stage k) -> slot k % 2 takes stage
+//             k + 2: 16 direct loads, one per 4 MFMAs over H0 rows 2-7 and
+//             H1 rows 0-1;
+//   end H0:   barrier B (stage k + 1 landed) -> its fragments are read
+//             during H1.
+// LDS chunk swizzle: chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16
+// rows of a fragment read (one 16-byte chunk per row) hit distinct banks and
+// a lane's fragment offsets differ by immediates across its blocks.
+// ---------------------------------------------------------------------------
+template <int DT> struct Mfma16;
+template <> struct Mfma16<NSG_F16> {
+  using T = _Float16;
+  using frag_t = f16x8;
+  static __device__ __forceinline__ f32x4 mma(frag_t a, frag_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma16<NSG_BF16> {
+  using T = __bf16;
+  using frag_t = bf16x8;
+  static __device__ __forceinline__ f32x4 mma(frag_t a, frag_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int DT, bool SYM>
+__global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
+  using MF = Mfma16<DT>;
+  using T = typename MF::T;
+  using frag_t = typename MF::frag_t;
+  constexpr int NW = 4;
+  constexpr int BK = 64;             // K elements per stage (128-byte row slices)
+  constexpr int SLICE = 256 * 128;   // bytes of one operand slice
+  constexpr int STAGE = 2 * SLICE;   // A slice then B slice
+  constexpr int NLD = 8;             // 1 KB direct loads per operand per wave per stage
+  constexpr int EPI_PITCH = 132;
+  constexpr int EPI_BYTES = 256 * EPI_PITCH * 4;
+  constexpr int LDS_BYTES = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES + 256];  // + prefetch sink
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int g, tm, tn;
+  tile_256<SYM>(p, g, tm, tn);
+
+  // direct-load sources: wave w fills the 1 KB blocks b = w + 4 i of each
+  // slice (rows 8 b .. 8 b + 7; lane l writes chunk slot l % 8 of row
+  // 8 b + l / 8, which holds logical chunk (l % 8) ^ ((row >> 1) & 7))
+  const T *gA = reinterpret_cast<const T *>(p.A) + (size_t)g * p.sA + (size_t)tm * 256 * p.lda;
+  const T *gB = reinterpret_cast<const T *>(p.B) + (size_t)g * p.sB + (size_t)tn * 256 * p.ldb;
+  unsigned offA[NLD], offB[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int row = (wave + NW * i) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    offA[i] = (unsigned)((row * (int)p.lda + chunk * 8) * 2);
+    offB[i] = (unsigned)((row * (int)p.ldb + chunk * 8) * 2);
+  }
+  const int nk = p.K / BK;  // >= 4: K is a multiple of 256
+  const T *pf_ptr = lane < 32 ? gA + (size_t)((tn & 7) + 8 * lane) * p.lda
+                              : gB + (size_t)((tm & 7) + 8 * (lane - 32)) * p.ldb;
+  auto prefetch = [&](int kt) {
+    if (wave == 0) lds_touch4(pf_ptr + (size_t)(kt < nk ? kt : nk - 1) * BK, lds + LDS_BYTES);
+  };
+  auto dma = [&](int kt, int slot, int q) {  // q-th of the 16 loads of a stage: pair q / 2, operand q % 2
+    unsigned char *st = lds + slot * STAGE;
+    const int i = q >> 1;
+    if (q & 1) lds_dma16(gB + (size_t)kt * BK, offB[i], st + SLICE + (wave + NW * i) * 1024);
+    else lds_dma16(gA + (size_t)kt * BK, offA[i], st + (wave + NW * i) * 1024);
+  };
+
+  // fragment reads: lane l reads row (block row + l % 16), K elements
+  // 32 s + 8 (l / 16) .. + 7 of the stage; block i adds i * 2048 bytes
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int rA = wm * 128 + r16, rB = wn * 128 + r16;
+  const int zA = (rA >> 1) & 7, zB = (rB >> 1) & 7;
+  const int fA0 = rA * 128 + ((q4 ^ zA) << 4), fA1 = rA * 128 + (((4 + q4) ^ zA) << 4);
+  const int fB0 = SLICE + rB * 128 + ((q4 ^ zB) << 4), fB1 = SLICE + rB * 128 + (((4 + q4) ^ zB) << 4);
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  frag_t a[8][2], b[8][2];
+  auto rd_a = [&](const unsigned char *st, int i) {
+    a[i][0] = *reinterpret_cast<const frag_t *>(st + fA0 + i * 2048);
+    a[i][1] = *reinterpret_cast<const frag_t *>(st + fA1 + i * 2048);
+  };
+  auto rd_b = [&](const unsigned char *st, int j) {
+    b[j][0] = *reinterpret_cast<const frag_t *>(st + fB0 + j * 2048);
+    b[j][1] = *reinterpret_cast<const frag_t *>(st + fB1 + j * 2048);
+  };
+  auto pair = [&](int i, int j) {
+    acc[i][j] = MF::mma(a[i][0], b[j][0], acc[i][j]);
+    acc[i][j] = MF::mma(a[i][1], b[j][1], acc[i][j]);
+  };
+
+#pragma unroll
+  for (int q = 0; q < 2 * NLD; ++q) dma(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < 2 * NLD; ++q) dma(1, 1, q);
+  wait_vmcnt<2 * NLD>();  // stage 0 landed
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rd_a(lds, i);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rd_b(lds, j);
+
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const unsigned char *nst = lds + ((kt + 1) & 1) * STAGE;
+    // past the end: stage nk-1 again, into the slot that is not read any
+    // more, so the wait counts stay uniform
+    const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+    const int dslot = kt & 1;
+    // ---- H0: columns 0-3 ----
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pair(i, j);
+        if (i >= 2 && (j & 1)) dma(kn, dslot, 2 * (i - 2) + (j >> 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i == 0) prefetch(kt + 2 + kPrefetchAhead);
+      if (i == 1) {
+        wait_lgkmcnt0();  // this wave's reads of stage kt are in registers
+        raw_barrier();    // A: ... and every other wave's: slot kt % 2 is free
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // this wave's loads of stage kt+1 landed (12 loads of stage kn and
+    // wave 0's prefetch may be in flight)
+    if (wave == 0) wait_vmcnt<13>();
+    else wait_vmcnt<12>();
+    raw_barrier();  // B: every wave's loads of stage kt+1 landed
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- H1: columns 4-7; the fragments of stage kt+1 replace those that died ----
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 4; j < 8; ++j) {
+        pair(i, j);
+        if (i < 2 && (j & 1)) dma(kn, dslot, 12 + 2 * i + ((j - 4) >> 1));
+        if (i == 0) rd_b(nst, j - 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      rd_a(nst, i);
+    }
+#pragma unroll
+    for (int j = 4; j < 8; ++j) rd_b(nst, j);
+  }
+  // last stage
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pair(i, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+  wait_vmcnt<0>();  // the last (unused) refill has landed
+  __syncthreads();  // all waves are done with the operand stages
+  staged_epilogue<T, SYM, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
 }
 
 int tile_m(int cfg) { return cfg == kTile256 ? 256 : 128; }
@@ -905,7 +1110,10 @@ static hipError_t launch_256(const GemmArgs &a, hipStream_t s) {
   const unsigned tiles = SYM ? tm * (tm + 1) / 2 : tm * tn;
   const unsigned long long blocks = (unsigned long long)tiles * (unsigned)a.batch;
   if (blocks == 0 || blocks > 0xFFFFFFFFull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm256_kernel<DT, SYM, kWaves256>), dim3((unsigned)blocks), dim3(kWaves256 * 64), 0, s, a);
+  if constexpr (DT == NSG_F32)
+    hipLaunchKernelGGL((gemm256_kernel<DT, SYM, kWaves256>), dim3((unsigned)blocks), dim3(kWaves256 * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm256h_kernel<DT, SYM>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
