@@ -372,20 +372,26 @@ template <typename V> __device__ __forceinline__ void st_stream(const V &v, V *p
 template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_type(16 / sizeof(TO)))); };
 
 // Epilogue of a 256x256 tile through LDS, in two passes of 128 rows.  The
-// fp32 tile is staged column-major (column c at c * PITCH floats, PITCH =
-// 132: A and B2 are free of LDS bank conflicts, B1's reads are 2-way).
-//   A: the waves owning the pass's rows write their accumulators, one
-//      16-byte write per 4 consecutive rows of a column.
-//   B1: a thread takes 1 row x 8 columns per step (a wave: 16 rows x 32
-//      columns, 64-byte row segments), forms v = alpha' acc + beta' Cin (0
-//      outside the valid corner) and stores out0 (and out2 = v + diag I)
-//      row-major; v goes back to LDS only when a transposed copy follows.
-//   B2: a thread takes 8 consecutive rows of one column (a wave: 64 rows x 8
-//      columns, 128-byte segments of 8 output rows) and stores the
-//      transposed copy: the mirror (j, i) of a symmetric product, or out1.
-// Inside a diagonal tile of a symmetric product only the lower half is
-// stored, to both places, so the output is exactly symmetric.  The
-// non-finite check of out0 runs only when a status array is given.
+// fp32 tile is staged column-major (column c at c * PITCH floats, PITCH = 132:
+// the staging writes are free of LDS bank conflicts).
+//   A: the waves owning the pass's rows write their accumulators.
+//   B: thread (rb, cb) = (lane % 8, lane / 8) of wave w owns two 8 x 8 blocks
+//      of the pass, at rows 64 (r & 1) + 8 rb and columns 64 (r >> 1) + 8 cb
+//      for regions r = w and w + 4.  It reads a block with 16-byte LDS reads
+//      (8 rows of one column each), forms v = alpha' acc + beta' Cin (Cin
+//      loaded before the staging, 8 rows of 16 bytes; v = 0 outside the valid
+//      Mv x Nv corner) and stores its 8 rows to out0 (and out2 = v + diag I)
+//      and its 8 columns to the transposed copy (the mirror of a symmetric
+//      product, or out1) as 16-byte vectors: the 8 lanes of equal rb (rows)
+//      or of equal cb (columns) fill 128-byte lines.  out0 writes zeros
+//      outside the valid corner when out0_pad, nothing otherwise; blocks that
+//      cross the corner, or an out0 that does not take 16-byte stores, store
+//      element by element.
+// Inside a diagonal tile of a symmetric product a block lies below the
+// diagonal (stored whole, to both places), above it (skipped: its mirror
+// partner stores it) or on it (its lower half, to both places), so the output
+// is exactly symmetric.  The non-finite check of out0 (valid elements only)
+// runs only when a status array is given.
 // Phase A writers: one wave's 128 x 128 accumulators into the column-major
 // staging area (16-byte writes of 4 consecutive rows of one column).
 // 32x32 MFMA tiles: lane l, register r = row 8 (r/4) + 4 (l/32) + r%4, column l%32.
@@ -417,8 +423,12 @@ template <typename T, typename TO, bool SYM, int NW, int PITCH, typename ACC>
 __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                   int tm, int tn, int wm, int wn, int lane, int tid) {
   static_assert(PITCH % 4 == 0, "16-byte staging writes");
+  static_assert(NW == 4, "two 8 x 8 blocks per thread and pass");
   constexpr int VT = 16 / (int)sizeof(T);   // elements of T per 16 bytes
   constexpr int VO = 16 / (int)sizeof(TO);  // elements of TO per 16 bytes
+  constexpr int NV = 8 / VT;                // 16-byte vectors of T per 8 elements
+  typedef typename Vec16<T>::type vt_t;
+  typedef typename Vec16<TO>::type vo_t;
   float sc = 1.f;
   if (p.gscale != nullptr && p.gpow > 0) {
     const float sg = p.gscale[g];
@@ -428,243 +438,140 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   const T *cin = p.Cin ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
   TO *o0 = p.out0 ? reinterpret_cast<TO *>(p.out0) + (size_t)g * p.s0 : nullptr;
   T *o1 = p.out1 ? reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1 : nullptr;
-  T *o2 = p.out2 ? reinterpret_cast<T *>(p.out2) + (size_t)g * p.s2 : nullptr;
+  T *o2 = (SYM && p.out2) ? reinterpret_cast<T *>(p.out2) + (size_t)g * p.s2 : nullptr;
+  T *ot = SYM ? reinterpret_cast<T *>(o0) : o1;  // transposed copy (symmetric outputs are in the compute dtype)
+  const int64_t ldt = SYM ? p.ld0 : p.ld1;
   const bool pad0 = p.out0_pad != 0;
   const bool chk = p.status != nullptr;
   const bool diag_tile = SYM && (tm == tn);
-  const bool transposed = SYM || o1 != nullptr;  // B2 runs
   // 16-byte row stores need the row pitch and base of out0 to allow them
   const bool vec0 = o0 != nullptr && (p.ld0 % VO) == 0 && ((reinterpret_cast<uintptr_t>(o0) & 15) == 0);
   const int wave = tid >> 6;
+  const int rb = lane & 7, cb = lane >> 3;
   bool finite = true;
+  vt_t cinv[2][8][NV];  // Cin of the thread's two blocks
+  auto load_cin = [&](int grow0, int gcol0, int it) {
+    const int reg = wave + 4 * it;
+    const T *cp = cin + (size_t)(grow0 + (reg & 1) * 64 + 8 * rb) * p.ldc + (gcol0 + (reg >> 1) * 64 + 8 * cb);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) cinv[it][r][e] = *reinterpret_cast<const vt_t *>(cp + (size_t)r * p.ldc + e * VT);
+  };
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int grow0 = tm * 256 + pass * 128;  // global row of staged row 0
     const int gcol0 = tn * 256;
-    const bool interior = grow0 + 128 <= p.Mv && gcol0 + 256 <= p.Nv;
+    if (cin != nullptr) load_cin(grow0, gcol0, 0);  // in flight during the staging
     // ---- A: accumulators -> LDS ----
     if (wm == pass) stage_acc<PITCH>(acc, lds, wn, lane);
     __syncthreads();
-    // ---- B1: row orientation ----
-    // Fast path: the whole pass is inside the valid corner, out0 takes 16-byte
-    // stores, the tile is off the diagonal and no status is checked, so no
-    // step needs a mask.
-    const bool fast = interior && (o0 == nullptr || vec0) && !diag_tile && !chk;
-    if (fast) {
-      auto b1 = [&](auto hc, auto tr, auto o2c) {
-        constexpr bool HC = decltype(hc)::value, TR = decltype(tr)::value, O2 = decltype(o2c)::value;
-        const int rs = lane & 15, cg = lane >> 4;
-        constexpr int U = 4;
-#pragma unroll 1
-        for (int k0 = 0; k0 < 64 / NW; k0 += U) {
-          float vv[U][8];
-          typename Vec16<T>::type cvv[U][8 / VT];
+    // ---- B: 8 x 8 blocks ----
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int it = wave + NW * (k0 + u);
-            const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
-            const float *src = lds + c * PITCH + r;
+    for (int it = 0; it < 2; ++it) {
+      if (it == 0 && cin != nullptr) load_cin(grow0, gcol0, 1);  // in flight during block 0
+      const int reg = wave + 4 * it;
+      const int rr = (reg & 1) * 64 + 8 * rb, cc = (reg >> 1) * 64 + 8 * cb;
+      const int grow = grow0 + rr, gcol = gcol0 + cc;
+      const bool full = grow + 8 <= p.Mv && gcol + 8 <= p.Nv;  // every element of the block is valid
+      float v[8][8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) vv[u][q] = src[q * PITCH];
-            if constexpr (HC) {
-              const T *cp = cin + (size_t)(grow0 + r) * p.ldc + (gcol0 + c);
+      for (int c = 0; c < 8; ++c) {
+        const float *src = lds + (cc + c) * PITCH + rr;
+        const float4 x0 = *reinterpret_cast<const float4 *>(src);
+        const float4 x1 = *reinterpret_cast<const float4 *>(src + 4);
+        v[0][c] = x0.x; v[1][c] = x0.y; v[2][c] = x0.z; v[3][c] = x0.w;
+        v[4][c] = x1.x; v[5][c] = x1.y; v[6][c] = x1.z; v[7][c] = x1.w;
+      }
 #pragma unroll
-              for (int e = 0; e < 8 / VT; ++e)
-                cvv[u][e] = *reinterpret_cast<const typename Vec16<T>::type *>(cp + e * VT);
-            }
-          }
+      for (int r = 0; r < 8; ++r)
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int it = wave + NW * (k0 + u);
-            const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
-            const size_t row = (size_t)(grow0 + r), col = (size_t)(gcol0 + c);
-            float v[8];
+        for (int c = 0; c < 8; ++c) {
+          float x = alpha * v[r][c];
+          if (cin != nullptr) x += beta * (float)cinv[it][r][c / VT][c % VT];
+          v[r][c] = x;
+        }
+      if (!full) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = alpha * vv[u][q];
-            if constexpr (HC) {
+        for (int r = 0; r < 8; ++r)
 #pragma unroll
-              for (int e = 0; e < 8 / VT; ++e)
+          for (int c = 0; c < 8; ++c)
+            if (!(grow + r < p.Mv && gcol + c < p.Nv)) v[r][c] = 0.f;
+      }
+      if (chk) {
 #pragma unroll
-                for (int q = 0; q < VT; ++q) v[e * VT + q] += beta * (float)cvv[u][e][q];
-            }
-            if constexpr (TR) {
-              float *src = lds + c * PITCH + r;
+        for (int r = 0; r < 8; ++r)
 #pragma unroll
-              for (int q = 0; q < 8; ++q) src[q * PITCH] = v[q];
-            }
-            if (o0 != nullptr) {
-              TO *dst = o0 + row * p.ld0 + col;
+          for (int c = 0; c < 8; ++c)
+            if (full || (grow + r < p.Mv && gcol + c < p.Nv))
+              finite = finite && __builtin_isfinite((float)cvt<TO>(v[r][c]));
+      }
+      // 0: off the diagonal or below it; 1: on it; 2: above it
+      const int cls = !diag_tile ? 0 : (grow >= gcol + 8 ? 0 : (grow == gcol ? 1 : 2));
+      // per-block bases; rows and columns step by uniform pitches
+      TO *const b0 = o0 + (size_t)grow * p.ld0 + gcol;
+      T *const bt = ot + (size_t)gcol * ldt + grow;
+      T *const b2r = o2 + (size_t)grow * p.ld2 + gcol;
+      T *const b2c = o2 + (size_t)gcol * p.ld2 + grow;
+      if (cls == 0) {
+        if (o0 != nullptr) {
+          if (vec0 && full) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
 #pragma unroll
               for (int e = 0; e < 8 / VO; ++e) {
-                typename Vec16<TO>::type w;
+                vo_t w;
 #pragma unroll
-                for (int q = 0; q < VO; ++q) w[q] = cvt<TO>(v[e * VO + q]);
-                st_stream(w, reinterpret_cast<typename Vec16<TO>::type *>(dst + e * VO));
+                for (int q = 0; q < VO; ++q) w[q] = cvt<TO>(v[r][e * VO + q]);
+                st_stream(w, reinterpret_cast<vo_t *>(b0 + (size_t)r * p.ld0 + e * VO));
               }
-            }
-            if constexpr (O2) {  // off the diagonal: out2 = v
-              T *dst = o2 + row * p.ld2 + col;
-#pragma unroll
-              for (int e = 0; e < 8 / VT; ++e) {
-                typename Vec16<T>::type w;
-#pragma unroll
-                for (int q = 0; q < VT; ++q) w[q] = cvt<T>(v[e * VT + q]);
-                st_stream(w, reinterpret_cast<typename Vec16<T>::type *>(dst + e * VT));
-              }
-            }
-          }
-        }
-      };
-      using TT = std::integral_constant<bool, true>;
-      using FF = std::integral_constant<bool, false>;
-      const bool has_o2 = SYM && o2 != nullptr;
-      if (cin != nullptr) {
-        if (transposed) { if (has_o2) b1(TT{}, TT{}, TT{}); else b1(TT{}, TT{}, FF{}); }
-        else b1(TT{}, FF{}, FF{});
-      } else {
-        if (transposed) { if (has_o2) b1(FF{}, TT{}, TT{}); else b1(FF{}, TT{}, FF{}); }
-        else b1(FF{}, FF{}, FF{});
-      }
-    } else {
-      const int rs = lane & 15, cg = lane >> 4;
-      constexpr int U = 4;  // steps whose LDS reads are issued together
-#pragma unroll 1
-      for (int k0 = 0; k0 < 64 / NW; k0 += U) {
-        float vv[U][8];
-        typename Vec16<T>::type cvv[U][8 / VT];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int it = wave + NW * (k0 + u);
-          const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
-          const float *src = lds + c * PITCH + r;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) vv[u][q] = src[q * PITCH];
-          if (cin != nullptr) {
-            const T *cp = cin + (size_t)(grow0 + r) * p.ldc + (gcol0 + c);
-#pragma unroll
-            for (int e = 0; e < 8 / VT; ++e) cvv[u][e] = *reinterpret_cast<const typename Vec16<T>::type *>(cp + e * VT);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-        const int it = wave + NW * (k0 + u);
-        const int r = (it >> 3) * 16 + rs, c = (it & 7) * 32 + cg * 8;
-        const int row = grow0 + r, col = gcol0 + c;
-        float *src = lds + c * PITCH + r;
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = alpha * vv[u][q];
-        if (cin != nullptr) {
-#pragma unroll
-          for (int e = 0; e < 8 / VT; ++e)
-#pragma unroll
-            for (int q = 0; q < VT; ++q) v[e * VT + q] += beta * (float)cvv[u][e][q];
-        }
-        const bool rv = row < p.Mv;
-        if (!interior) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (!(rv && col + q < p.Nv)) v[q] = 0.f;
-        }
-        if (transposed) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) src[q * PITCH] = v[q];
-        }
-        const bool all_valid = interior || (rv && col + 8 <= p.Nv);
-        if (o0 != nullptr) {
-          TO h[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) h[q] = cvt<TO>(v[q]);
-          if (chk) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if (all_valid || (rv && col + q < p.Nv)) finite = finite && __builtin_isfinite((float)h[q]);
-          }
-          TO *dst = o0 + (size_t)row * p.ld0 + col;
-          // in a diagonal tile a group of 8 is wholly below the diagonal
-          // (row >= col + 7), wholly above it (row < col: stored by the
-          // mirror) or straddles it (masked element stores)
-          if (diag_tile && row < col) {
-          } else if (vec0 && (!diag_tile || row >= col + 7) && (all_valid || pad0)) {
-#pragma unroll
-            for (int e = 0; e < 8 / VO; ++e) {
-              typename Vec16<TO>::type w;
-#pragma unroll
-              for (int q = 0; q < VO; ++q) w[q] = h[e * VO + q];
-              st_stream(w, reinterpret_cast<typename Vec16<TO>::type *>(dst + e * VO));
-            }
           } else {
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if ((pad0 || (rv && col + q < p.Nv)) && (!diag_tile || row >= col + q)) st_stream(h[q], dst + q);
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+              for (int c = 0; c < 8; ++c)
+                if (pad0 || (grow + r < p.Mv && gcol + c < p.Nv))
+                  st_stream(cvt<TO>(v[r][c]), b0 + (size_t)r * p.ld0 + c);
           }
         }
-        if constexpr (SYM) {
-          if (o2 != nullptr) {
-            T h[8];
+        if (o2 != nullptr) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) h[q] = cvt<T>((row == col + q && rv) ? v[q] + p.diag : v[q]);
-            T *dst = o2 + (size_t)row * p.ld2 + col;
-            if (diag_tile && row < col) {
-            } else if (!diag_tile || row >= col + 7) {
+          for (int r = 0; r < 8; ++r)
 #pragma unroll
-              for (int e = 0; e < 8 / VT; ++e) {
-                typename Vec16<T>::type w;
+            for (int e = 0; e < NV; ++e) {
+              vt_t w;
 #pragma unroll
-                for (int q = 0; q < VT; ++q) w[q] = h[e * VT + q];
-                st_stream(w, reinterpret_cast<typename Vec16<T>::type *>(dst + e * VT));
-              }
-            } else {
+              for (int q = 0; q < VT; ++q) w[q] = cvt<T>(v[r][e * VT + q]);
+              st_stream(w, reinterpret_cast<vt_t *>(b2r + (size_t)r * p.ld2 + e * VT));
+            }
+        }
+        if (ot != nullptr) {  // columns: the transposed copy (and out2's mirror)
 #pragma unroll
-              for (int q = 0; q < 8; ++q)
-                if (row >= col + q) st_stream(h[q], dst + q);
+          for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int e = 0; e < NV; ++e) {
+              vt_t w;
+#pragma unroll
+              for (int q = 0; q < VT; ++q) w[q] = cvt<T>(v[e * VT + q][c]);
+              st_stream(w, reinterpret_cast<vt_t *>(bt + (size_t)c * ldt + e * VT));
+              if (o2 != nullptr) st_stream(w, reinterpret_cast<vt_t *>(b2c + (size_t)c * p.ld2 + e * VT));
+            }
+        }
+      } else if (cls == 1) {  // on the diagonal: the lower half, to both places
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int c = 0; c <= r; ++c) {
+            if (o0 != nullptr) st_stream(cvt<TO>(v[r][c]), b0 + (size_t)r * p.ld0 + c);
+            if (r > c) st_stream(cvt<T>(v[r][c]), bt + (size_t)c * ldt + r);
+            if (o2 != nullptr) {
+              const T d = cvt<T>((r == c && grow + r < p.Mv) ? v[r][c] + p.diag : v[r][c]);
+              st_stream(d, b2r + (size_t)r * p.ld2 + c);
+              if (r > c) st_stream(d, b2c + (size_t)c * p.ld2 + r);
             }
           }
-        }
-        }
       }
-    }
-    if (transposed) {
-      __syncthreads();
-      // ---- B2: column orientation (transposed copy) ----
-      T *ot = SYM ? reinterpret_cast<T *>(o0) : o1;  // symmetric outputs are in the compute dtype
-      const int ldt = SYM ? (int)p.ld0 : (int)p.ld1;
-      const int rg = lane & 7, cc = lane >> 3;
-#pragma unroll 1
-      for (int k = 0; k < 2; ++k) {
-        T *dstbase = (k == 0) ? ot : (SYM ? o2 : nullptr);
-        const int ldk = (k == 0) ? ldt : (int)p.ld2;
-        if (dstbase == nullptr) continue;
-#pragma unroll 4
-        for (int it = wave; it < 64; it += NW) {
-          const int r = (it >> 5) * 64 + rg * 8, c = (it & 31) * 8 + cc;
-          const int row = grow0 + r, col = gcol0 + c;
-          const float *src = lds + c * PITCH + r;
-          const float4 f0 = *reinterpret_cast<const float4 *>(src);
-          const float4 f1 = *reinterpret_cast<const float4 *>(src + 4);
-          const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-          T h[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) h[q] = cvt<T>(v[q]);
-          T *dst = dstbase + (size_t)col * ldk + row;
-          // diagonal tile: rows row..row+7 of column col go to the upper half
-          // only where row + q > col
-          if (diag_tile && row + 7 <= col) {
-          } else if (!diag_tile || row > col) {
-#pragma unroll
-            for (int u = 0; u < 8 / VT; ++u) {
-              typename Vec16<T>::type w;
-#pragma unroll
-              for (int q = 0; q < VT; ++q) w[q] = h[u * VT + q];
-              st_stream(w, reinterpret_cast<typename Vec16<T>::type *>(dst + u * VT));
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if (row + q > col) st_stream(h[q], dst + q);
-          }
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (pass == 0) __syncthreads();  // LDS is rewritten by the next pass
   }
