@@ -32,7 +32,7 @@ bool valid_dtype(int dt) { return dt == NSG_F16 || dt == NSG_BF16 || dt == NSG_F
 // Workspace buffers, each [G][rows][cols] in the compute dtype unless noted.
 enum Buf : int {
   kPartials = 0,  // fp32 [G][nchunks]
-  kGScale,        // fp32 [G]
+  kGScale,        // fp32 [G] residual scale r, then int32 [G] exponent e
   kX0,            // np x mp   (X0 scaled by 2^e)
   kX0T,           // mp x np
   kX1,            // np x mp   (X after the restart / standard ping-pong)
@@ -300,7 +300,7 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     if (!P.used[i]) { P.off[i] = 0; continue; }
     size_t per;
     if (i == kPartials) per = (size_t)P.nchunks * 4;
-    else if (i == kGScale) per = 4;
+    else if (i == kGScale) per = 8;  // r (fp32), then e (int32) in a second [G] array
     else per = (size_t)P.rows[i] * P.ld[i] * dtype_size(P.cdtype);
     P.off[i] = off;
     off = align_up(off + per * (size_t)G, NSG_WORKSPACE_ALIGN);

@@ -82,7 +82,7 @@ struct ScaleArgs {
   int64_t ld_same = 0, ld_swap = 0;  // row pitches (elements)
   int64_t s_same = 0, s_swap = 0;    // elements per matrix
   int32_t cdtype = NSG_F16;
-  float *gscale = nullptr;
+  float *gscale = nullptr;   // [G] r, followed by [G] int32 e
   int32_t *status = nullptr;
   int32_t batch = 0;
 };

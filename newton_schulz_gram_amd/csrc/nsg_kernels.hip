@@ -1109,33 +1109,42 @@ hipError_t launch_norm_reduce(const NormReduceArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Scale by an exact power of two, cast, and write both layouts through a
-// 64x64 LDS tile.  Every block recomputes the norm from the partial sums in
-// the same fixed order, so all blocks of a matrix agree bit for bit.  Each
-// thread moves 16 consecutive elements of a row: one or two 16-byte loads when
-// the input rows allow it (VEC), else scalar loads; the same values either
-// way.  Outputs (workspace, 128-byte-aligned pitches) use 16-byte stores.
+// Per matrix: nu = sqrt(sum of the partial sums, fixed tree), kappa =
+// 1 / (s (nu + eps)), kappa 2^f = r 2^e with r in [0.5, 1): gscale[g] = r,
+// gscale[G + g] = e (int32), status[g] = 0.
+__global__ void __launch_bounds__(256) scale_finalize_kernel(const ScaleArgs p) {
+  __shared__ float red[4];
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  float s = 0.f;
+  for (int i = tid; i < p.nchunks; i += 256) s += p.partials[(size_t)g * p.nchunks + i];
+  s = block_sum_256(s, red);
+  if (tid == 0) {
+    const float nu = sqrtf(s);
+    const float kappa = 1.f / (p.safety * (nu + p.eps));
+    int e = 0;
+    const float r = frexpf(ldexpf(kappa, p.fexp), &e);
+    p.gscale[g] = r;
+    reinterpret_cast<int32_t *>(p.gscale + p.batch)[g] = e;
+    if (p.status != nullptr) p.status[g] = 0;
+  }
+}
+
+// Scale by the exact power of two 2^e, cast, and write both layouts through a
+// 64x64 LDS tile.  Each thread moves 16 consecutive elements of a row: one or
+// two 16-byte loads when the input rows allow it (VEC), else scalar loads; the
+// same values either way.  Outputs (workspace, 128-byte-aligned pitches) use
+// 16-byte stores.
 template <typename TI, typename TO, bool VEC>
 __global__ void __launch_bounds__(256) scale_cast_transpose_kernel(const ScaleArgs p) {
   __shared__ float tile[64][65];
-  __shared__ float red[4];
   constexpr int VI = 16 / (int)sizeof(TI);
   constexpr int VO = 16 / (int)sizeof(TO);
   typedef TI vin_t __attribute__((ext_vector_type(VI)));
   typedef TO vout_t __attribute__((ext_vector_type(VO)));
   const int g = blockIdx.z;
   const int tid = threadIdx.x;
-  float s = 0.f;
-  for (int i = tid; i < p.nchunks; i += 256) s += p.partials[(size_t)g * p.nchunks + i];
-  s = block_sum_256(s, red);
-  const float nu = sqrtf(s);
-  const float kappa = 1.f / (p.safety * (nu + p.eps));
-  int e = 0;
-  const float r = frexpf(ldexpf(kappa, p.fexp), &e);  // kappa 2^f = r 2^e, r in [0.5, 1)
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
-    p.gscale[g] = r;
-    if (p.status != nullptr) p.status[g] = 0;
-  }
+  const int e = reinterpret_cast<const int32_t *>(p.gscale + p.batch)[g];
   const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 64;
   const TI *in = reinterpret_cast<const TI *>(p.in) + (size_t)g * (size_t)(p.R * p.C);
   // load: thread -> row tid / 4, columns 16 (tid % 4) .. + 15
@@ -1196,6 +1205,7 @@ static void launch_scale_in(const ScaleArgs &a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_scale(const ScaleArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(scale_finalize_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
   dim3 grid((unsigned)(a.cols_p / 64), (unsigned)(a.rows_p / 64), (unsigned)a.batch);
   const size_t es = a.in_dtype == NSG_F32 ? 4 : 2;
   const bool vec = (reinterpret_cast<uintptr_t>(a.in) % 16 == 0) && ((size_t)a.C * es) % 16 == 0;
