@@ -53,7 +53,7 @@ def algorithmic_flops(entry, G):
 def kernel_kind(symbol: str):
     if "copy_kernel" in symbol:
         return "copy"
-    if "gemm256_kernel" in symbol or "gemm_nt_kernel" in symbol:
+    if "gemm256" in symbol or "gemm_nt_kernel" in symbol:
         return "gemm_nt_sym" if ", true" in symbol else "gemm_nt"
     if "norm_reduce_kernel" in symbol:
         return "norm_reduce"
