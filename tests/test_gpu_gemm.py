@@ -93,3 +93,29 @@ def test_symmetric_product_of_distinct_operands_is_mirrored(tile):
     low = torch.tril(torch.ones(n, n, device="cuda", dtype=torch.bool))
     assert torch.equal(out, out.transpose(1, 2))
     assert rel(out[:, low], ref[:, low]) <= TOL[torch.float16]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("kind,batch,n", [("sym", 3, 4096), ("sym", 2, 4352), ("gen", 5, 2048)])
+def test_tile_schedule_covers_every_tile(dtype, kind, batch, n):
+    """More 256 x 256 tiles than CUs and not a multiple of them (408, 306, 320
+    tiles), and a triangle whose last row of 8 x 8-tile super-blocks is partial
+    (17 tile rows): the persistent workgroups must produce every tile once."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    K = 256
+    A = torch.randn(batch, n, K, device="cuda", generator=g).to(dtype)
+    if kind == "sym":
+        out, _, _ = nsg.gemm_nt(A, A, symmetric=True, tile=256)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out.transpose(1, 2))
+        ref = ref_nt(A, A)
+    else:
+        B = torch.randn(batch, n, K, device="cuda", generator=g).to(dtype)
+        out, _, _ = nsg.gemm_nt(A, B, tile=256)
+        torch.cuda.synchronize()
+        ref = ref_nt(A, B)
+    assert rel(out, ref) <= TOL[dtype]
+    # no tile left unwritten or mixed up: every 256 x 256 block matches on its own
+    d = (out.float() - ref).view(batch, n // 256, 256, n // 256, 256).norm(dim=(2, 4))
+    r = ref.view(batch, n // 256, 256, n // 256, 256).norm(dim=(2, 4))
+    assert float((d / r).max()) <= 4 * TOL[dtype]
