@@ -113,11 +113,19 @@ def cpu_baseline(w, x_cpu, budget_s: float = 30.0):
 
     import oracle
 
-    threads = None
+    threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((d.get("num_threads") or 0) for d in threadpool_info()) or None
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"] or threadpool_info()
+        threads = max((d.get("num_threads") or 0) for d in info) or None
+        blas = ", ".join(sorted({f"{d.get('internal_api')} {d.get('version') or ''}".strip() for d in info}))
     except Exception:
+        pass
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
         pass
     done, t0 = 0, time.perf_counter()
     while done < w.G:
@@ -130,7 +138,8 @@ def cpu_baseline(w, x_cpu, budget_s: float = 30.0):
     return {"value": done / dt, "unit": "matrices/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
             "sample": f"{done} of {w.G} matrices ({w.R}x{w.C}), full NS in fp64 numpy, {dt:.1f} s",
-            "seconds_per_matrix": dt / done}
+            "seconds_per_matrix": dt / done, "blas": blas, "cpu_model": cpu_model,
+            "host_cpu_count": os.cpu_count()}
 
 
 def bench_select(args, w, dev):
@@ -307,12 +316,16 @@ def main():
 
     nsg.timing_enable(True)
     nsg.timing_collect()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     recs = nsg.timing_collect()
     nsg.timing_enable(False)
 
@@ -371,6 +384,8 @@ def main():
                    "mode": w.mode, "steps": w.steps, "restart_after": w.restart_after,
                    "safety": w.safety, "coeffs": list(w.coeffs), "accumulate": "f32",
                    "sym_updates": not args.general_updates},
+        "ms_per_call_median": round(per_call[len(per_call) // 2], 3),
+        "ms_per_call_iqr": round(per_call[(3 * len(per_call)) // 4] - per_call[len(per_call) // 4], 3),
         "effective_tflops": round(eff_tflops, 2),
         "pct_fp16_peak": round(100 * eff_tflops / PEAK_FP16_TFLOPS, 2),
         "executed_tflops": round(executed * w.G * args.steps / wall / 1e12, 2),
