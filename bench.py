@@ -32,10 +32,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernels and the launch plan with comments and blank space
+    removed, so that only a change of the code voids stored counter data."""
+    import re
+
     h = hashlib.sha256()
     for f in ("nsg_kernels.hip", "nsg_internal.h", "nsg_api.cpp"):  # kernels and the launch plan
-        with open(os.path.join(ROOT, "newton_schulz_gram_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "newton_schulz_gram_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,7 +1,8 @@
 // gfx950 (MI355X) kernels for batched Newton–Schulz orthogonalization.
 //
-//  * gemm_nt_kernel: batched C = A B^T on MFMA (fp16/bf16 32x32x16, fp32
-//    32x32x2), fp32 accumulation, LDS double buffering, and a fused fp32
+//  * gemm256h_kernel (fp16/bf16, 16x16x32 MFMAs), gemm256_kernel (fp32,
+//    32x32x2) and gemm_nt_kernel (128 x 128 tiles for small n): batched
+//    C = A B^T, fp32 accumulation, LDS double buffering, and a fused fp32
 //    epilogue (alpha acc + beta Cin, per-matrix scale, optional transposed
 //    store, optional "+ diag * I" second store, non-finite flag).  The
 //    symmetric variant runs only tiles on or below the diagonal and writes
@@ -308,7 +309,8 @@ gemm_nt_kernel(const GemmArgs p) {
 #undef NSG_SWRITE
 
 // ---------------------------------------------------------------------------
-// 256x256 batched NT GEMM for large matrices.  NW waves (2 along M), each
+// 256x256 batched NT GEMM for large matrices on 32x32 MFMA tiles (the fp32
+// path; fp16 / bf16 use gemm256h_kernel below).  NW waves (2 along M), each
 // owning a 128 x (512/NW) block of 32x32 MFMA tiles (NW = 4: 128x128, 256
 // fp32 accumulators per lane).  Operands stream global -> LDS with direct
 // loads (global_load_lds_dwordx4, no register staging) in stages of 128-byte
@@ -324,9 +326,9 @@ gemm_nt_kernel(const GemmArgs p) {
 // the swizzle spreads an MFMA fragment read of 16 (or 8) consecutive rows at
 // one chunk over distinct banks.
 //
-// Tile order: within a matrix, tiles go in groups of 4 tile rows (column by
-// column); the block id -> tile map below gives each XCD 32 consecutive tiles
-// of that order at a time, all XCDs working on the same matrix.
+// Tile order: tile_256 below (groups of 4 tile rows for general products,
+// 8 x 8-tile super-blocks of the lower triangle for symmetric ones; each XCD
+// takes 32 consecutive tiles of that order at a time).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int slice_swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_slice_off(int r, int c) { return r * 128 + ((c ^ slice_swz(r)) << 4); }
