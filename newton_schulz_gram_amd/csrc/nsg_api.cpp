@@ -359,7 +359,11 @@ void ns_default_params(nsg_params_t *p) {
 }
 
 const char *ns_status_string(nsg_status_t s) {
-  switch (s) {
+  // a C caller may pass any int: read it as one (an out-of-range value held in
+  // the enum type would be undefined in C++)
+  int v = 0;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case NSG_OK: return "ok";
     case NSG_ERR_INVALID_ARG: return "invalid argument";
     case NSG_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
