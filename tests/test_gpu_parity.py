@@ -204,6 +204,26 @@ def test_non_finite_input_sets_status():
     assert torch.isfinite(out[0]).all() and torch.isfinite(out[2]).all()
 
 
+def test_naive_gram_blow_up_raises_status():
+    """Gram NS without a restart (Dion3 paper, Algorithm 2) in fp16 on a rank-16
+    matrix, run for T = 10 steps: the spurious eigenvalues of the iterated Gram
+    matrix grow until the output is non-finite (the pages' App. B failure
+    mode), and the status flag reports it without a host synchronisation.  The
+    recommended setup (T = 5, restart before step 3) on the same matrix stays
+    finite and clear."""
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy((rng.standard_normal((512, 16)) @ rng.standard_normal((16, 2048))).astype(np.float32))
+    x = x[None].half().cuda()
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = nsg.orthogonalize(x, steps=10, mode="gram", restart_after=0, compute_dtype=torch.float16, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 1 and not bool(torch.isfinite(y.float()).all())
+    st[0] = 7
+    y = nsg.orthogonalize(x, steps=5, mode="gram", restart_after=2, compute_dtype=torch.float16, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0 and bool(torch.isfinite(y.float()).all())
+
+
 def test_in_place_and_output_dtype():
     x = custom(2, 200, 500, "f16", "gaussian", seed=31)
     ref = oracle_of(x)
