@@ -380,8 +380,9 @@ template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_
 //   B: thread (rb, cb) = (lane % 8, lane / 8) of wave w owns two 8 x 8 blocks
 //      of the pass, at rows 64 (r & 1) + 8 rb and columns 64 (r >> 1) + 8 cb
 //      for regions r = w and w + 4.  It reads a block with 16-byte LDS reads
-//      (8 rows of one column each), forms v = alpha' acc + beta' Cin (Cin
-//      loaded before the staging, 8 rows of 16 bytes; v = 0 outside the valid
+//      (8 rows of one column each), forms v = alpha' acc + beta' Cin (Cin:
+//      8 rows of 16 bytes per block, the first block loaded before the
+//      staging, the second at the start of the first; v = 0 outside the valid
 //      Mv x Nv corner) and stores its 8 rows to out0 (and out2 = v + diag I)
 //      and its 8 columns to the transposed copy (the mirror of a symmetric
 //      product, or out1) as 16-byte vectors: the 8 lanes of equal rb (rows)
@@ -389,6 +390,10 @@ template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_
 //      outside the valid corner when out0_pad, nothing otherwise; blocks that
 //      cross the corner, or an out0 that does not take 16-byte stores, store
 //      element by element.
+// CIN (Cin given) is a template argument: with a run-time test, the wait
+// counts the compiler derives for the Cin loads merge with those of a path
+// without them, and the first block then waits for loads issued just before
+// it.
 // Inside a diagonal tile of a symmetric product a block lies below the
 // diagonal (stored whole, to both places), above it (skipped: its mirror
 // partner stores it) or on it (its lower half, to both places), so the output
@@ -421,7 +426,7 @@ __device__ __forceinline__ void stage_acc(const f32x4 (&acc)[8][TN], float *lds,
           make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
 }
 
-template <typename T, typename TO, bool SYM, int NW, int PITCH, typename ACC>
+template <typename T, typename TO, bool SYM, bool CIN, int NW, int PITCH, typename ACC>
 __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                   int tm, int tn, int wm, int wn, int lane, int tid) {
   static_assert(PITCH % 4 == 0, "16-byte staging writes");
@@ -437,7 +442,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
     sc = (p.gpow == 1) ? sg : sg * sg;
   }
   const float alpha = p.alpha * sc, beta = p.beta * sc;
-  const T *cin = p.Cin ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
+  const T *cin = CIN ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
   TO *o0 = p.out0 ? reinterpret_cast<TO *>(p.out0) + (size_t)g * p.s0 : nullptr;
   T *o1 = p.out1 ? reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1 : nullptr;
   T *o2 = (SYM && p.out2) ? reinterpret_cast<T *>(p.out2) + (size_t)g * p.s2 : nullptr;
@@ -451,10 +456,11 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   const int wave = tid >> 6;
   const int rb = lane & 7, cb = lane >> 3;
   bool finite = true;
-  vt_t cinv[2][8][NV];  // Cin of the thread's two blocks
-  auto load_cin = [&](int grow0, int gcol0, int it) {
+  vt_t cinv[2][8][NV];  // Cin of the thread's block it of a pass
+  auto load_cin = [&](int pass, int it) {
     const int reg = wave + 4 * it;
-    const T *cp = cin + (size_t)(grow0 + (reg & 1) * 64 + 8 * rb) * p.ldc + (gcol0 + (reg >> 1) * 64 + 8 * cb);
+    const T *cp = cin + (size_t)(tm * 256 + pass * 128 + (reg & 1) * 64 + 8 * rb) * p.ldc +
+                  (tn * 256 + (reg >> 1) * 64 + 8 * cb);
 #pragma unroll
     for (int r = 0; r < 8; ++r)
 #pragma unroll
@@ -464,14 +470,14 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   for (int pass = 0; pass < 2; ++pass) {
     const int grow0 = tm * 256 + pass * 128;  // global row of staged row 0
     const int gcol0 = tn * 256;
-    if (cin != nullptr) load_cin(grow0, gcol0, 0);  // in flight during the staging
+    if constexpr (CIN) load_cin(pass, 0);
     // ---- A: accumulators -> LDS ----
     if (wm == pass) stage_acc<PITCH>(acc, lds, wn, lane);
     __syncthreads();
     // ---- B: 8 x 8 blocks ----
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      if (it == 0 && cin != nullptr) load_cin(grow0, gcol0, 1);  // in flight during block 0
+      if constexpr (CIN) { if (it == 0) load_cin(pass, 1); }
       const int reg = wave + 4 * it;
       const int rr = (reg & 1) * 64 + 8 * rb, cc = (reg >> 1) * 64 + 8 * cb;
       const int grow = grow0 + rr, gcol = gcol0 + cc;
@@ -490,7 +496,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           float x = alpha * v[r][c];
-          if (cin != nullptr) x += beta * (float)cinv[it][r][c / VT][c % VT];
+          if constexpr (CIN) x += beta * (float)cinv[it][r][c / VT][c % VT];
           v[r][c] = x;
         }
       if (!full) {
@@ -580,18 +586,18 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   if (chk && __ballot(!finite) != 0 && lane == 0) p.status[g] = 1;
 }
 
-template <typename T, bool SYM, int NW, int PITCH, typename ACC>
+template <typename T, bool SYM, bool CIN, int NW, int PITCH, typename ACC>
 __device__ __forceinline__ void staged_epilogue(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                 int tm, int tn, int wm, int wn, int lane, int tid) {
   if constexpr (SYM) {
-    staged_epilogue_t<T, T, true, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+    staged_epilogue_t<T, T, true, CIN, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   } else {
     if (p.out0_dtype == NSG_F16)
-      staged_epilogue_t<T, _Float16, false, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, _Float16, false, CIN, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
     else if (p.out0_dtype == NSG_BF16)
-      staged_epilogue_t<T, __bf16, false, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, __bf16, false, CIN, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
     else
-      staged_epilogue_t<T, float, false, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, float, false, CIN, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   }
 }
 
@@ -815,7 +821,10 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
   // ---- fp32 epilogue (same contract as gemm_nt_kernel), staged in LDS ----
   wait_vmcnt<0>();  // the last (unused) refill has landed
   __syncthreads();  // all waves are done with the operand stages
-  staged_epilogue<T, SYM, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
+  if (p.Cin != nullptr)
+    staged_epilogue<T, SYM, true, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
+  else
+    staged_epilogue<T, SYM, false, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
 }
 
 
@@ -859,7 +868,7 @@ template <> struct Mfma16<NSG_BF16> {
   }
 };
 
-template <int DT, bool SYM>
+template <int DT, bool SYM, bool CIN>
 __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   using MF = Mfma16<DT>;
   using T = typename MF::T;
@@ -1004,7 +1013,7 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 
   wait_vmcnt<0>();  // the last (unused) refill has landed
   __syncthreads();  // all waves are done with the operand stages
-  staged_epilogue<T, SYM, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
+  staged_epilogue<T, SYM, CIN, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
   __syncthreads();  // the staging area is read before the next tile's loads overwrite it
   }
 }
@@ -1066,7 +1075,10 @@ static hipError_t launch_256(const GemmArgs &a, hipStream_t s) {
     const unsigned ncu = cu_count();
     if (ncu == 0) return hipErrorInvalidDevice;
     const unsigned grid = blocks < ncu ? (unsigned)blocks : ncu;
-    hipLaunchKernelGGL((gemm256h_kernel<DT, SYM>), dim3(grid), dim3(256), 0, s, a);
+    if (a.Cin != nullptr)
+      hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, false>), dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
