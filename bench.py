@@ -257,6 +257,39 @@ def bench_muon(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def bench_blas(args, w, dev):
+    """Calibration only: the vendor BLAS (torch.matmul) on the bucket's product shapes, fp16 operands,
+    full products (it has no symmetric or fused forms). Not part of the library's path."""
+    import torch
+    torch.manual_seed(0)
+    G, n, m = w.G, min(w.R, w.C), max(w.R, w.C)
+    rnd = lambda *s: (torch.randn(*s, device=dev) * 0.5).half()
+
+    def timed(f, reps):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    Q, X = rnd(G, n, n), rnd(G, n, m)
+    Xt = X.transpose(1, 2).contiguous()
+    cases = [("Q X (n x n times n x m)", lambda: torch.matmul(Q, X), 2.0 * G * n * n * m),
+             ("X X^T (n x m times m x n)", lambda: torch.matmul(X, Xt), 2.0 * G * n * n * m),
+             ("Q Q (n x n times n x n)", lambda: torch.matmul(Q, Q), 2.0 * G * n ** 3)]
+    res = {}
+    for name, f, fl in cases:
+        ms = timed(f, max(args.steps, 1))
+        res[name] = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
+                     "pct_fp16_peak": round(100.0 * fl / ms / 1e9 / PEAK_FP16_TFLOPS, 1)}
+    print(json.dumps({"vendor_blas_fp16": res, "workload": w.name, "G": G, "n": n, "m": m}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +303,8 @@ def main():
                     help="time the whole Muon step (momentum, orthogonalization, update) on the bucket")
     ap.add_argument("--general-updates", action="store_true",
                     help="run Q Z + a Q and R Z + a R as general products (default: symmetric kernel)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="calibration: time the vendor BLAS (torch.matmul) on the bucket's product shapes")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run the library copy kernel over COPY_BYTES (byte-counter calibration)")
@@ -295,6 +330,8 @@ def main():
         return bench_select(args, w, dev)
     if args.muon_step:
         return bench_muon(args, w, dev)
+    if args.blas_reference:
+        return bench_blas(args, w, dev)
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     t_gen = time.perf_counter()

@@ -1253,11 +1253,81 @@ __global__ void __launch_bounds__(256) scale_cast_transpose_kernel(const ScaleAr
   }
 }
 
+// The same scale, cast and transpose for 16-bit outputs, on 64 x 128 input
+// tiles: each thread loads 8 consecutive inputs of 4 rows (16 lanes cover a
+// 128-element row segment), writes them in the input layout straight from
+// registers, and parks the converted values in LDS (row pitch 65 words:
+// conflict-free 4-byte writes and column reads).  The transposed copy is then
+// written as 128-byte rows: a thread takes two adjacent input columns (one
+// 4-byte LDS word per row) and 8 input rows.  Every output element is
+// cvt(ldexp(x, e)), as in the kernel above.
+template <typename TI, typename TO, bool VEC>
+__global__ void __launch_bounds__(256) scale_cast_transpose16_kernel(const ScaleArgs p) {
+  static_assert(sizeof(TO) == 2, "16-bit outputs");
+  constexpr int PW = 65;  // LDS row pitch in 32-bit words (two outputs each)
+  __shared__ uint32_t tile[64 * PW];
+  constexpr int VI = 16 / (int)sizeof(TI);
+  typedef TI vin_t __attribute__((ext_vector_type(VI)));
+  typedef TO vout_t __attribute__((ext_vector_type(8)));
+  typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+  const int g = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int e = reinterpret_cast<const int32_t *>(p.gscale + p.batch)[g];
+  const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 128;
+  const TI *in = reinterpret_cast<const TI *>(p.in) + (size_t)g * (size_t)(p.R * p.C);
+  TO *same = reinterpret_cast<TO *>(p.same) + (size_t)g * p.s_same;
+  TO *swp = reinterpret_cast<TO *>(p.swap) + (size_t)g * p.s_swap;
+  const int cl = (tid & 15) * 8;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int a = (tid >> 4) + 16 * k, row = a0 + a, col = b0 + cl;
+    float v[8];
+    if (VEC && row < p.R && col + 8 <= p.C) {
+      const TI *src = in + (size_t)row * p.C + col;
+#pragma unroll
+      for (int u = 0; u < 8 / VI; ++u) {
+        const vin_t x = *reinterpret_cast<const vin_t *>(src + u * VI);
+#pragma unroll
+        for (int q = 0; q < VI; ++q) v[u * VI + q] = to_f32(x[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[q] = (row < p.R && col + q < p.C) ? to_f32(in[(size_t)row * p.C + col + q]) : 0.f;
+    }
+    vout_t w;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = cvt<TO>(ldexpf(v[q], e));
+    *reinterpret_cast<vout_t *>(same + (size_t)row * p.ld_same + col) = w;
+    const u16x8 bits = __builtin_bit_cast(u16x8, w);
+    uint32_t *t = tile + a * PW + (cl >> 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = (uint32_t)bits[2 * u] | ((uint32_t)bits[2 * u + 1] << 16);
+  }
+  __syncthreads();
+  const int ac = 8 * (tid & 7);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int bp = 2 * (tid >> 3) + 64 * h;  // input columns bp, bp + 1 of the tile
+    u16x8 lo, hi;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t x = tile[(ac + q) * PW + (bp >> 1)];
+      lo[q] = (unsigned short)(x & 0xFFFFu);
+      hi[q] = (unsigned short)(x >> 16);
+    }
+    *reinterpret_cast<vout_t *>(swp + (size_t)(b0 + bp) * p.ld_swap + (a0 + ac)) = __builtin_bit_cast(vout_t, lo);
+    *reinterpret_cast<vout_t *>(swp + (size_t)(b0 + bp + 1) * p.ld_swap + (a0 + ac)) = __builtin_bit_cast(vout_t, hi);
+  }
+}
+
 template <typename TI, bool VEC>
 static void launch_scale_in(const ScaleArgs &a, dim3 grid, hipStream_t s) {
+  // 16-bit outputs: 64 x 128 tiles (the padded column count is a multiple of 256)
+  const dim3 grid16(grid.x / 2, grid.y, grid.z);
   switch (a.cdtype) {
-    case NSG_F16: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, _Float16, VEC>), grid, dim3(256), 0, s, a); break;
-    case NSG_BF16: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, __bf16, VEC>), grid, dim3(256), 0, s, a); break;
+    case NSG_F16: hipLaunchKernelGGL((scale_cast_transpose16_kernel<TI, _Float16, VEC>), grid16, dim3(256), 0, s, a); break;
+    case NSG_BF16: hipLaunchKernelGGL((scale_cast_transpose16_kernel<TI, __bf16, VEC>), grid16, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, float, VEC>), grid, dim3(256), 0, s, a); break;
   }
 }
