@@ -61,10 +61,14 @@ def kernel_kind(symbol: str):
     if "copy_kernel" in symbol:
         return "copy"
     if "gemm256" in symbol or "gemm_nt_kernel" in symbol:
-        return "gemm_nt_sym" if ", true" in symbol else "gemm_nt"
+        # the symmetric flag: second template argument of gemm256h_kernel<DT, SYM, CIN> and
+        # gemm256_kernel<DT, SYM, NW>, last of gemm_nt_kernel<DT, BM, BN, WGM, WGN, SYM>
+        targs = [t.strip() for t in symbol[symbol.index("<") + 1:symbol.index(">")].split(",")]
+        sym = targs[-1] if "gemm_nt_kernel" in symbol else targs[1]
+        return "gemm_nt_sym" if sym in ("true", "1") else "gemm_nt"
     if "norm_reduce_kernel" in symbol:
         return "norm_reduce"
-    if "scale_cast_transpose_kernel" in symbol:
+    if "scale_cast_transpose" in symbol:
         return "scale_cast_transpose"
     return None
 
