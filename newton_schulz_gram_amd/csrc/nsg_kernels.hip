@@ -911,8 +911,10 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   const int nk = p.K / BK;  // >= 4: K is a multiple of 256
   const T *pf_ptr = lane < 32 ? gA + (size_t)((tn & 7) + 8 * lane) * p.lda
                               : gB + (size_t)((tm & 7) + 8 * (lane - 32)) * p.ldb;
+  // lanes 16 w .. 16 w + 15 of wave w touch their lines, so every wave issues
+  // one touch per stage and the waves reach the barriers evenly loaded
   auto prefetch = [&](int kt) {
-    if (wave == 0) lds_touch4(pf_ptr + (size_t)(kt < nk ? kt : nk - 1) * BK, lds + LDS_BYTES);
+    if ((lane >> 4) == wave) lds_touch4(pf_ptr + (size_t)(kt < nk ? kt : nk - 1) * BK, lds + LDS_BYTES);
   };
   auto dma = [&](int kt, int slot, int q) {  // q-th of the 16 loads of a stage: pair q / 2, operand q % 2
     unsigned char *st = lds + slot * STAGE;
@@ -981,10 +983,9 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // this wave's loads of stage kt+1 landed (12 loads of stage kn and
-    // wave 0's prefetch may be in flight)
-    if (wave == 0) wait_vmcnt<13>();
-    else wait_vmcnt<12>();
+    // this wave's loads of stage kt+1 landed (12 loads of stage kn and the
+    // prefetch touch may be in flight)
+    wait_vmcnt<13>();
     raw_barrier();  // B: every wave's loads of stage kt+1 landed
     __builtin_amdgcn_sched_barrier(0);
     // ---- H1: columns 4-7; the fragments of stage kt+1 replace those that died ----
