@@ -11,10 +11,11 @@
 //    symmetric (Dion3 paper, Section 5 "Triangular Scheduler" and "Epilogue:
 //    Writing to the Transposed Tile"; Appendix C.1 on writing diagonal tiles
 //    once).
-//  * norm_reduce_kernel / scale_cast_transpose_kernel: the Frobenius
-//    normalization X / (s (||X||_F + eps)) and the cast to the compute dtype
-//    (Dion3 paper, Alg. 3 steps 2-3), written both as X (n x m) and X^T, with
-//    zero padding.
+//  * norm_reduce_kernel, scale_finalize_kernel and scale_cast_transpose16_kernel
+//    (16-bit compute dtypes) / scale_cast_transpose_kernel (fp32): the
+//    Frobenius normalization X / (s (||X||_F + eps)) and the cast to the
+//    compute dtype (Dion3 paper, Alg. 3 steps 2-3), written both as X (n x m)
+//    and X^T, with zero padding.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
