@@ -882,7 +882,7 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   constexpr int EPI_PITCH = 132;
   constexpr int EPI_BYTES = 256 * EPI_PITCH * 4;
   constexpr int LDS_BYTES = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES + 256];  // + prefetch sink
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -910,13 +910,6 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
     offB[i] = (unsigned)((row * (int)p.ldb + chunk * 8) * 2);
   }
   const int nk = p.K / BK;  // >= 4: K is a multiple of 256
-  const T *pf_ptr = lane < 32 ? gA + (size_t)((tn & 7) + 8 * lane) * p.lda
-                              : gB + (size_t)((tm & 7) + 8 * (lane - 32)) * p.ldb;
-  // lanes 16 w .. 16 w + 15 of wave w touch their lines, so every wave issues
-  // one touch per stage and the waves reach the barriers evenly loaded
-  auto prefetch = [&](int kt) {
-    if ((lane >> 4) == wave) lds_touch4(pf_ptr + (size_t)(kt < nk ? kt : nk - 1) * BK, lds + LDS_BYTES);
-  };
   auto dma = [&](int kt, int slot, int q) {  // q-th of the 16 loads of a stage: pair q / 2, operand q % 2
     unsigned char *st = lds + slot * STAGE;
     const int i = q >> 1;
@@ -977,16 +970,15 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
         if (i >= 2 && (j & 1)) dma(kn, dslot, 2 * (i - 2) + (j >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (i == 0) prefetch(kt + 2 + kPrefetchAhead);
       if (i == 1) {
         wait_lgkmcnt0();  // this wave's reads of stage kt are in registers
         raw_barrier();    // A: ... and every other wave's: slot kt % 2 is free
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // this wave's loads of stage kt+1 landed (12 loads of stage kn and the
-    // prefetch touch may be in flight)
-    wait_vmcnt<13>();
+    // this wave's loads of stage kt+1 landed (the 12 loads of stage kn issued
+    // so far in this stage may be in flight)
+    wait_vmcnt<12>();
     raw_barrier();  // B: every wave's loads of stage kt+1 landed
     __builtin_amdgcn_sched_barrier(0);
     // ---- H1: columns 4-7; the fragments of stage kt+1 replace those that died ----
