@@ -844,8 +844,8 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
 // as they die: a stage runs columns 0-3 (H0) then columns 4-7 (H1), row by
 // row, so B columns 0-3 are free during H1, A row i after H1 row i, and B
 // columns 4-7 at the end.  LDS slot use per stage k (slot k % 2):
-//   H0 row 1: barrier A (every wave read stage k) -> slot k % 2 takes stage
-//             k + 2: 16 direct loads, one per 4 MFMAs over H0 rows 2-7 and
+//   H0 row 0: barrier A (every wave read stage k) -> slot k % 2 takes stage
+//             k + 2: 16 direct loads, one per 4 MFMAs over H0 rows 1-6 and
 //             H1 rows 0-1;
 //   end H0:   barrier B (stage k + 1 landed) -> its fragments are read
 //             during H1.
@@ -967,10 +967,10 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         pair(i, j);
-        if (i >= 2 && (j & 1)) dma(kn, dslot, 2 * (i - 2) + (j >> 1));
+        if (i >= 1 && i <= 6 && (j & 1)) dma(kn, dslot, 2 * (i - 1) + (j >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (i == 1) {
+      if (i == 0) {
         wait_lgkmcnt0();  // this wave's reads of stage kt are in registers
         raw_barrier();    // A: ... and every other wave's: slot kt % 2 is free
         __builtin_amdgcn_sched_barrier(0);
