@@ -845,8 +845,8 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
 // row, so B columns 0-3 are free during H1, A row i after H1 row i, and B
 // columns 4-7 at the end.  LDS slot use per stage k (slot k % 2):
 //   H0 row 0: barrier A (every wave read stage k) -> slot k % 2 takes stage
-//             k + 2: 16 direct loads, one per 4 MFMAs over H0 rows 1-6 and
-//             H1 rows 0-1;
+//             k + 2: 16 direct loads, one per 4 MFMAs over H0 rows 1-4 and
+//             H1 rows 0-3;
 //   end H0:   barrier B (stage k + 1 landed) -> its fragments are read
 //             during H1.
 // LDS chunk swizzle: chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16
@@ -967,7 +967,7 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         pair(i, j);
-        if (i >= 1 && i <= 6 && (j & 1)) dma(kn, dslot, 2 * (i - 1) + (j >> 1));
+        if (i >= 1 && i <= 4 && (j & 1)) dma(kn, dslot, 2 * (i - 1) + (j >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i == 0) {
@@ -976,9 +976,9 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // this wave's loads of stage kt+1 landed (the 12 loads of stage kn issued
+    // this wave's loads of stage kt+1 landed (the 8 loads of stage kn issued
     // so far in this stage may be in flight)
-    wait_vmcnt<12>();
+    wait_vmcnt<8>();
     raw_barrier();  // B: every wave's loads of stage kt+1 landed
     __builtin_amdgcn_sched_barrier(0);
     // ---- H1: columns 4-7; the fragments of stage kt+1 replace those that died ----
@@ -987,7 +987,7 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 #pragma unroll
       for (int j = 4; j < 8; ++j) {
         pair(i, j);
-        if (i < 2 && (j & 1)) dma(kn, dslot, 12 + 2 * i + ((j - 4) >> 1));
+        if (i < 4 && (j & 1)) dma(kn, dslot, 8 + 2 * i + ((j - 4) >> 1));
         if (i == 0) rd_b(nst, j - 4);
         __builtin_amdgcn_sched_barrier(0);
       }
