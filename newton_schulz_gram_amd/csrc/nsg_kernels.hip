@@ -847,8 +847,8 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
 //   H0 row 0: barrier A (every wave read stage k) -> slot k % 2 takes stage
 //             k + 2: 16 direct loads, one per 4 MFMAs over H0 rows 1-4 and
 //             H1 rows 0-3;
-//   end H0:   barrier B (stage k + 1 landed) -> its fragments are read
-//             during H1.
+//   H1 row 0: barrier B (stage k + 1 landed) -> its fragments are read
+//             during the rest of H1.
 // LDS chunk swizzle: chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16
 // rows of a fragment read (one 16-byte chunk per row) hit distinct banks and
 // a lane's fragment offsets differ by immediates across its blocks.
@@ -976,19 +976,22 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // this wave's loads of stage kt+1 landed (the 8 loads of stage kn issued
-    // so far in this stage may be in flight)
-    wait_vmcnt<8>();
-    raw_barrier();  // B: every wave's loads of stage kt+1 landed
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- H1: columns 4-7; the fragments of stage kt+1 replace those that died ----
+    // ---- H1: columns 4-7; the fragments of stage kt+1 replace those that
+    //      died (B columns 0-3 during row 1, A row i after row i) ----
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int j = 4; j < 8; ++j) {
         pair(i, j);
         if (i < 4 && (j & 1)) dma(kn, dslot, 8 + 2 * i + ((j - 4) >> 1));
-        if (i == 0) rd_b(nst, j - 4);
+        if (i == 1) rd_b(nst, j - 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i == 0) {
+        // this wave's loads of stage kt+1 landed (the 10 loads of stage kn
+        // issued so far in this stage may be in flight)
+        wait_vmcnt<10>();
+        raw_barrier();  // B: every wave's loads of stage kt+1 landed
         __builtin_amdgcn_sched_barrier(0);
       }
       rd_a(nst, i);
