@@ -955,11 +955,12 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) rd_b(lds, j);
 
-  for (int kt = 0; kt + 1 < nk; ++kt) {
+  // one 64-element stage: compute stage kt from registers, read stage kt+1's
+  // fragments, and (REFILL) load stage kt+2 into the slot stage kt leaves
+  auto step = [&](int kt, auto refill) {
+    constexpr bool REFILL = decltype(refill)::value;
     const unsigned char *nst = lds + ((kt + 1) & 1) * STAGE;
-    // past the end: stage nk-1 again, into the slot that is not read any
-    // more, so the wait counts stay uniform
-    const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+    const int kn = kt + 2;
     const int dslot = kt & 1;
     // ---- H0: columns 0-3 ----
 #pragma unroll
@@ -967,10 +968,10 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         pair(i, j);
-        if (i >= 1 && i <= 4 && (j & 1)) dma(kn, dslot, 2 * (i - 1) + (j >> 1));
+        if (REFILL && i >= 1 && i <= 4 && (j & 1)) dma(kn, dslot, 2 * (i - 1) + (j >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (i == 0) {
+      if (REFILL && i == 0) {
         wait_lgkmcnt0();  // this wave's reads of stage kt are in registers
         raw_barrier();    // A: ... and every other wave's: slot kt % 2 is free
         __builtin_amdgcn_sched_barrier(0);
@@ -983,14 +984,15 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 #pragma unroll
       for (int j = 4; j < 8; ++j) {
         pair(i, j);
-        if (i < 4 && (j & 1)) dma(kn, dslot, 8 + 2 * i + ((j - 4) >> 1));
+        if (REFILL && i < 4 && (j & 1)) dma(kn, dslot, 8 + 2 * i + ((j - 4) >> 1));
         if (i == 1) rd_b(nst, j - 4);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i == 0) {
-        // this wave's loads of stage kt+1 landed (the 10 loads of stage kn
-        // issued so far in this stage may be in flight)
-        wait_vmcnt<10>();
+        // this wave's loads of stage kt+1 landed (with REFILL, the 10 loads
+        // of stage kt+2 issued so far in this stage may be in flight)
+        if (REFILL) wait_vmcnt<10>();
+        else wait_vmcnt<0>();
         raw_barrier();  // B: every wave's loads of stage kt+1 landed
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -998,7 +1000,9 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
     }
 #pragma unroll
     for (int j = 4; j < 8; ++j) rd_b(nst, j);
-  }
+  };
+  for (int kt = 0; kt + 2 < nk; ++kt) step(kt, std::true_type{});
+  step(nk - 2, std::false_type{});  // no stage nk to load
   // last stage
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -1008,7 +1012,6 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-  wait_vmcnt<0>();  // the last (unused) refill has landed
   __syncthreads();  // all waves are done with the operand stages
   staged_epilogue<T, SYM, CIN, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
   __syncthreads();  // the staging area is read before the next tile's loads overwrite it
