@@ -375,8 +375,12 @@ template <typename V> __device__ __forceinline__ void st_stream(const V &v, V *p
 template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_type(16 / sizeof(TO)))); };
 
 // Epilogue of a 256x256 tile through LDS, in two passes of 128 rows.  The
-// fp32 tile is staged column-major (column c at c * PITCH floats, PITCH = 132:
-// the staging writes are free of LDS bank conflicts).
+// fp32 tile is staged column-major: column c at c * PITCH floats (PITCH =
+// 132), its rows rotated by stage_rot(c) (+4 or -4 rows modulo 128 when bit 3
+// of c is set, by bit 0).  The staging writes (16 consecutive columns, one
+// 4-row chunk, per 16 lanes) and the block reads below (16 lanes = columns c
+// and c + 8, 8 row chunks) then both hit 16 distinct 4-bank groups; without
+// the rotation the reads collide 2-way.
 //   A: the waves owning the pass's rows write their accumulators.
 //   B: thread (rb, cb) = (lane % 8, lane / 8) of wave w owns two 8 x 8 blocks
 //      of the pass, at rows 64 (r & 1) + 8 rb and columns 64 (r >> 1) + 8 cb
@@ -403,27 +407,33 @@ template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_
 // Phase A writers: one wave's 128 x 128 accumulators into the column-major
 // staging area (16-byte writes of 4 consecutive rows of one column).
 // 32x32 MFMA tiles: lane l, register r = row 8 (r/4) + 4 (l/32) + r%4, column l%32.
+// Row rotation of a staged column: columns with bit 3 set move their rows by
+// +4 (bit 0 clear) or -4 (bit 0 set), modulo 128.
+__device__ __forceinline__ int stage_rot(int col) { return (col & 8) ? ((col & 1) ? -4 : 4) : 0; }
 template <int PITCH, int TN>
 __device__ __forceinline__ void stage_acc(const f32x16 (&acc)[4][TN], float *lds, int wn, int lane) {
+  const int sw = stage_rot(lane);  // the low 5 bits of the lane's column are lane % 32
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      float *col = lds + (wn * TN * 32 + j * 32 + (lane & 31)) * PITCH + i * 32 + 4 * (lane >> 5);
+      float *col = lds + (wn * TN * 32 + j * 32 + (lane & 31)) * PITCH;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<float4 *>(col + 8 * r4) = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+        *reinterpret_cast<float4 *>(col + ((i * 32 + 4 * (lane >> 5) + 8 * r4 + sw) & 127)) = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
                                                                 acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
     }
 }
 // 16x16 MFMA tiles: lane l, register r = row 4 (l/16) + r, column l%16.
 template <int PITCH, int TN>
 __device__ __forceinline__ void stage_acc(const f32x4 (&acc)[8][TN], float *lds, int wn, int lane) {
+  const int sw = stage_rot(lane);  // the low 4 bits of the lane's column are lane % 16
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      *reinterpret_cast<float4 *>(lds + (wn * TN * 16 + j * 16 + (lane & 15)) * PITCH + i * 16 + 4 * (lane >> 4)) =
+      *reinterpret_cast<float4 *>(lds + (wn * TN * 16 + j * 16 + (lane & 15)) * PITCH +
+                                  ((i * 16 + 4 * (lane >> 4) + sw) & 127)) =
           make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
 }
 
@@ -486,9 +496,10 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
       float v[8][8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float *src = lds + (cc + c) * PITCH + rr;
-        const float4 x0 = *reinterpret_cast<const float4 *>(src);
-        const float4 x1 = *reinterpret_cast<const float4 *>(src + 4);
+        const float *src = lds + (cc + c) * PITCH;
+        const int rot = (cb & 1) ? ((c & 1) ? -4 : 4) : 0;  // stage_rot(cc + c)
+        const float4 x0 = *reinterpret_cast<const float4 *>(src + ((rr + rot) & 127));
+        const float4 x1 = *reinterpret_cast<const float4 *>(src + ((rr + 4 + rot) & 127));
         v[0][c] = x0.x; v[1][c] = x0.y; v[2][c] = x0.z; v[3][c] = x0.w;
         v[4][c] = x1.x; v[5][c] = x1.y; v[6][c] = x1.z; v[7][c] = x1.w;
       }
