@@ -857,7 +857,7 @@ __global__ void __launch_bounds__(NW * 64, 1) gemm256_kernel(const GemmArgs p) {
 // columns 4-7 at the end.  LDS slot use per stage k (slot k % 2):
 //   H0 row 0: barrier A (every wave read stage k) -> slot k % 2 takes stage
 //             k + 2: 16 direct loads, one per 4 MFMAs over H0 rows 1-4 and
-//             H1 rows 0-3;
+//             H1 rows 1-4;
 //   H1 row 0: barrier B (stage k + 1 landed) -> its fragments are read
 //             during the rest of H1.
 // LDS chunk swizzle: chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16
@@ -995,14 +995,14 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 #pragma unroll
       for (int j = 4; j < 8; ++j) {
         pair(i, j);
-        if (REFILL && i < 4 && (j & 1)) dma(kn, dslot, 8 + 2 * i + ((j - 4) >> 1));
+        if (REFILL && i >= 1 && i <= 4 && (j & 1)) dma(kn, dslot, 8 + 2 * (i - 1) + ((j - 4) >> 1));
         if (i == 1) rd_b(nst, j - 4);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i == 0) {
-        // this wave's loads of stage kt+1 landed (with REFILL, the 10 loads
-        // of stage kt+2 issued so far in this stage may be in flight)
-        if (REFILL) wait_vmcnt<10>();
+        // this wave's loads of stage kt+1 landed (with REFILL, the 8 loads
+        // of stage kt+2 issued in the first half may be in flight)
+        if (REFILL) wait_vmcnt<8>();
         else wait_vmcnt<0>();
         raw_barrier();  // B: every wave's loads of stage kt+1 landed
         __builtin_amdgcn_sched_barrier(0);
