@@ -420,8 +420,8 @@ __device__ __forceinline__ void stage_acc(const f32x16 (&acc)[4][TN], float *lds
       float *col = lds + (wn * TN * 32 + j * 32 + (lane & 31)) * PITCH;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<float4 *>(col + ((i * 32 + 4 * (lane >> 5) + 8 * r4 + sw) & 127)) = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
-                                                                acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
+        *reinterpret_cast<float4 *>(col + ((i * 32 + 4 * (lane >> 5) + 8 * r4 + sw) & 127)) =
+            make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
     }
 }
 // 16x16 MFMA tiles: lane l, register r = row 4 (l/16) + r, column l%16.
