@@ -9,8 +9,13 @@ GEMM of Algorithm 3 or 1, output), inputs resident in HBM.  Prints one JSON
 line: matrices/s (whole job), effective TFLOP/s from the pages' FLOP formula
 and its fraction of the fp16 dense MFMA peak, a roofline object for the
 dominant kernel (per-launch durations from HIP events recorded by the library
-on the stream its kernels run on), and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+on the stream its kernels run on), the fp64 CPU oracle timed on a bounded
+sample of the same workload, a parity object comparing the GPU output with
+those oracle outputs, and (default workload only) the same figures for the
+other four buckets under "other_configs", each against the roofline that
+bounds it (MFMA for the 4096-wide buckets, HBM for the GPT-2-small and MoE
+buckets, whose algorithmic intensity is below the ridge point).
+Progress lines go to stderr; stdout carries the one JSON line.
 """
 from __future__ import annotations
 
@@ -25,6 +30,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "matrices/s and effective TFLOP/s (% fp16 MFMA peak), Gram NS, 7B bucket"
+# metric label and the roofline that bounds each bucket (the HBM-bound ones
+# sit below the ridge point, 2516.6 TFLOP/s / 8 TB/s = 315 FLOP/B)
+WORKLOAD_INFO = {
+    "llama7b_mlp_32x11008x4096_bf16": (METRIC, "mfma"),
+    "square_32x4096x4096_f16": ("matrices/s and effective TFLOP/s (% fp16 MFMA peak), standard NS "
+                                "(square fallback), 32x4096x4096 fp16 bucket", "mfma"),
+    "gpt2s_mlp_42x768x3072_f16": ("matrices/s and effective TFLOP/s (% of HBM roofline), Gram NS, "
+                                  "GPT-2-small MLP bucket 42x768x3072 fp16", "hbm"),
+    "moe_512x2048x512_f16": ("matrices/s and effective TFLOP/s (% of HBM roofline), Gram NS, "
+                             "MoE expert bucket 512x2048x512 fp16", "hbm"),
+    "single_1x128x512_f32": ("calls/s, Gram NS, single fp32 128x512 matrix (launch-latency bound)", "latency"),
+}
+OTHER_CONFIGS = ("gpt2s_mlp_42x768x3072_f16", "square_32x4096x4096_f16", "moe_512x2048x512_f16",
+                 "single_1x128x512_f32")
+# matrices of each bucket the parity sample compares with the oracle (a
+# bounded set: the oracle is fp64 numpy on the host)
+PARITY_SAMPLE = {"gpt2s_mlp_42x768x3072_f16": list(range(0, 42, 3)), "square_32x4096x4096_f16": [0],
+                 "moe_512x2048x512_f16": list(range(0, 512, 32)), "single_1x128x512_f32": [0]}
 PEAK_FP16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz (dense)
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "llama7b_mlp_32x11008x4096_bf16"
@@ -117,13 +140,11 @@ def ingest_pmc(fetch_csv, write_csv, workload):
     print(json.dumps(tr[workload]))
 
 
-def cpu_baseline(w, x_cpu, budget_s: float = 30.0):
-    """The oracle as it stands, on a bounded sample: whole matrices of the bucket,
-    stopping once the time budget is spent (at least one matrix)."""
-    import numpy as np
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
 
-    import oracle
 
+def host_info():
     threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
@@ -138,19 +159,61 @@ def cpu_baseline(w, x_cpu, budget_s: float = 30.0):
             cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
     except OSError:
         pass
-    done, t0 = 0, time.perf_counter()
+    return threads, blas, cpu_model
+
+
+def oracle_outputs(w, x_cpu, idx):
+    """The oracle on matrices idx of the bucket (fp64 numpy, as it stands)."""
+    import oracle
+
+    return oracle.orthogonalize(x_cpu[idx].double().numpy(), w.steps, w.coeffs, w.mode, w.restart_after,
+                                w.safety)
+
+
+def cpu_baseline(w, x_cpu, budget_s: float = 30.0):
+    """The oracle as it stands, on a bounded sample: whole matrices of the bucket,
+    stopping once half the time budget is spent (at least one matrix).
+    Returns (baseline object, sample indices, oracle outputs)."""
+    import numpy as np
+
+    threads, blas, cpu_model = host_info()
+    outs, done, t0 = [], 0, time.perf_counter()
     while done < w.G:
-        oracle.orthogonalize(x_cpu[done:done + 1].double().numpy(), w.steps, w.coeffs, w.mode,
-                             w.restart_after, w.safety)
+        outs.append(oracle_outputs(w, x_cpu, [done])[0])
         done += 1
         if time.perf_counter() - t0 > budget_s / 2:
             break
     dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "matrices/s", "cores": threads or os.cpu_count(),
+    base = {"value": done / dt, "unit": "matrices/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
             "sample": f"{done} of {w.G} matrices ({w.R}x{w.C}), full NS in fp64 numpy, {dt:.1f} s",
             "seconds_per_matrix": dt / done, "blas": blas, "cpu_model": cpu_model,
             "host_cpu_count": os.cpu_count()}
+    return base, list(range(done)), np.stack(outs)
+
+
+def parity_object(out_gpu, idx, ref, classes=None):
+    """GPU output of matrices idx against the oracle's: worst relative
+    Frobenius error, cosine, 256 x 256 block error and element error (the
+    measures of the GPU parity tests), plus whether the pages' bars hold;
+    with `classes` (matrix index -> conditioning class) also the worst
+    relative error per class."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity_metrics import bucket_errors, summary
+
+    o = out_gpu[idx].float().cpu()
+    errs = bucket_errors(o, ref)
+    sm = summary(errs)
+    res = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in sm.items()}
+    res["matrices"] = idx if len(idx) <= 8 else f"{len(idx)} of the bucket: {idx[0]}..{idx[-1]}"
+    res["within_bars"] = bool(sm["rel_max"] <= 3e-2 and sm["cos_min"] >= 0.97)
+    if classes is not None:
+        per = {}
+        for g, e in zip(idx, errs):
+            c = classes(g)
+            per[c] = round(max(per.get(c, 0.0), e["rel"]), 6)
+        res["rel_max_per_class"] = per
+    return res
 
 
 def bench_select(args, w, dev):
@@ -164,9 +227,7 @@ def bench_select(args, w, dev):
     torch.cuda.set_device(dev)
     x = synth.make(w).to(dev)
     G, R, C = x.shape
-    dim = 1 if C < R else 0
-    n_sel = C if dim == 1 else R
-    k = nsg.select_count(n_sel, args.select_fraction)
+    dim, k = nsg.select_plan(R, C, args.select_fraction)
     kw = dict(steps=w.steps, coeffs=w.coeffs, mode=w.mode, restart_after=w.restart_after, safety=w.safety,
               compute_dtype=w.compute, sym_updates=not args.general_updates)
     out = torch.empty_like(x)
@@ -294,6 +355,136 @@ def bench_blas(args, w, dev):
     print(json.dumps({"vendor_blas_fp16": res, "workload": w.name, "G": G, "n": n, "m": m}), flush=True)
 
 
+def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False):
+    """Warm up, then time `steps` whole calls with per-launch HIP events from the
+    library; returns (result dict, input on the host, GPU output)."""
+    import torch
+
+    import newton_schulz_gram_amd as nsg
+    import synth
+
+    t_gen = time.perf_counter()
+    x_cpu = synth.make(w)
+    t_gen = time.perf_counter() - t_gen
+    x = x_cpu.to(dev)
+    out = torch.empty_like(x)
+    kw = dict(steps=w.steps, coeffs=w.coeffs, mode=w.mode, restart_after=w.restart_after,
+              safety=w.safety, compute_dtype=w.compute, sym_updates=sym_updates)
+    ws = torch.empty(nsg.workspace_size(w.G, w.R, w.C, **kw), dtype=torch.uint8, device=dev)
+    status = torch.zeros(w.G, dtype=torch.int32, device=dev)
+    plan = nsg.plan(w.R, w.C, **kw)
+    credited, executed = nsg.flops(w.R, w.C, **kw)
+
+    if calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            nsg.copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(warmup):
+        nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
+    torch.cuda.synchronize()
+
+    nsg.timing_enable(True)
+    nsg.timing_collect()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    recs = nsg.timing_collect()
+    nsg.timing_enable(False)
+
+    value = w.G * steps / wall
+    eff_tflops = credited * w.G * steps / wall / 1e12
+
+    # per-launch durations, matched to the plan (same launch order every step)
+    per = len(plan)
+    assert len(recs) == per * steps, (len(recs), per, steps)
+    by_kernel = {}
+    for i, (name, ms) in enumerate(recs):
+        e = plan[i % per]
+        d = by_kernel.setdefault(name, {"ms": 0.0, "launches": 0, "algo_flops": 0.0, "bytes": 0.0})
+        d["ms"] += ms
+        d["launches"] += 1
+        d["algo_flops"] += algorithmic_flops(e, w.G)
+        d["bytes"] += e["bytes"] * w.G
+    bytes_per_matrix = sum(e["bytes"] for e in plan)
+    label, bound = WORKLOAD_INFO.get(w.name, (f"matrices/s, {w.mode} NS, {w.name}", "mfma"))
+    dominant = max((k for k in by_kernel if k.startswith("gemm")), key=lambda k: by_kernel[k]["ms"])
+    d = by_kernel[dominant]
+    avg_ms = d["ms"] / d["launches"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get(w.name, {}).get(dominant)
+            if ent and ent.get("kernel_src") == kernel_source_hash():
+                traffic = ent.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    common = {"kernel": dominant, "traffic": traffic, "avg_launch_ms": round(avg_ms, 4),
+              "launches_per_step": d["launches"] // steps}
+    if bound == "hbm":
+        achieved = d["bytes"] / d["launches"] / (avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), **common,
+                    "algo_bytes_per_launch": d["bytes"] / d["launches"]}
+    else:
+        achieved = d["algo_flops"] / d["launches"] / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), **common,
+                    "algo_flops_per_launch": d["algo_flops"] / d["launches"]}
+    # normalize pass: reads the input twice (norm, then scale) and writes X0 once
+    in_bytes = x.numel() * x.element_size()
+    x0_bytes = w.G * w.n * w.m * (4 if w.compute == "f32" else 2)
+    norm_ms = sum(by_kernel.get(k, {"ms": 0})["ms"] for k in ("norm_reduce", "scale_cast_transpose"))
+    kernels = {k: {"ms_per_step": round(v["ms"] / steps, 3),
+                   "tflops_algo": round(v["algo_flops"] / (v["ms"] * 1e-3) / 1e12, 1) if v["algo_flops"] else None,
+                   "gbs_algo": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
+               for k, v in by_kernel.items()}
+    # whole call against the HBM roofline of its algorithmic bytes
+    hbm_roof_mps = PEAK_HBM_GBS * 1e9 / bytes_per_matrix
+    res = {
+        "metric": label,
+        "value": round(value, 3),
+        "unit": "matrices/s",
+        "ms_per_step": round(1e3 * wall / steps, 3),
+        "ms_per_call_median": round(per_call[len(per_call) // 2], 3),
+        "ms_per_call_iqr": round(per_call[(3 * len(per_call)) // 4] - per_call[len(per_call) // 4], 3),
+        "effective_tflops": round(eff_tflops, 2),
+        "pct_fp16_peak": round(100 * eff_tflops / PEAK_FP16_TFLOPS, 2),
+        "executed_tflops": round(executed * w.G * steps / wall / 1e12, 2),
+        "flops_per_matrix": {"credited": credited, "executed": executed},
+        "algo_bytes_per_matrix": bytes_per_matrix,
+        "hbm_roofline": {"matrices_per_s": round(hbm_roof_mps, 1),
+                         "tflops": round(credited * hbm_roof_mps / 1e12, 1),
+                         "frac": round(value / hbm_roof_mps, 4)},
+        "normalize": {"ms_per_step": round(norm_ms / steps, 3),
+                      "algo_bytes": 2 * in_bytes + x0_bytes,
+                      "gbs": round((2 * in_bytes + x0_bytes) / (norm_ms / steps * 1e-3) / 1e9, 1) if norm_ms else None},
+        "kernels": kernels,
+        "roofline": roofline,
+        "nonfinite_matrices": int(status.sum().item()),
+        "input_gen_s": round(t_gen, 1),
+        "steps": steps,
+        "warmup": warmup,
+        "config": {"workload": w.name, "G": w.G, "R": w.R, "C": w.C, "input_dtype": w.dtype,
+                   "mode": w.mode if w.R != w.C else "standard (square fallback)", "steps": w.steps,
+                   "restart_after": w.restart_after, "safety": w.safety, "coeffs": list(w.coeffs),
+                   "compute": w.compute, "accumulate": "f32", "sym_updates": sym_updates},
+    }
+    del ws, x
+    return res, x_cpu, out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +492,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time only the named workload (default: the other four buckets too)")
     ap.add_argument("--select-fraction", type=float, default=None,
                     help="time the Dion3 selection front-end: k = ceil(f n) lines of the smaller dimension")
     ap.add_argument("--muon-step", action="store_true",
@@ -325,7 +518,6 @@ def main():
 
     import torch
 
-    import newton_schulz_gram_amd as nsg
     import synth
 
     w = synth.WORKLOADS[args.workload]
@@ -338,116 +530,46 @@ def main():
         return bench_blas(args, w, dev)
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
-    t_gen = time.perf_counter()
-    x_cpu = synth.make(w)
-    t_gen = time.perf_counter() - t_gen
-    x = x_cpu.to(dev)
-    out = torch.empty_like(x)
-    kw = dict(steps=w.steps, coeffs=w.coeffs, mode=w.mode, restart_after=w.restart_after,
-              safety=w.safety, compute_dtype=w.compute, sym_updates=not args.general_updates)
-    ws = torch.empty(nsg.workspace_size(w.G, w.R, w.C, **kw), dtype=torch.uint8, device=dev)
-    status = torch.zeros(w.G, dtype=torch.int32, device=dev)
-    plan = nsg.plan(w.R, w.C, **kw)
-    credited, executed = nsg.flops(w.R, w.C, **kw)
-
-    if args.calibrate_copy:
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            nsg.copy(src, dst)
-        torch.cuda.synchronize()
-        del src, dst
-
-    for _ in range(args.warmup):
-        nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
-    torch.cuda.synchronize()
-
-    nsg.timing_enable(True)
-    nsg.timing_collect()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record()
-    for i in range(args.steps):
-        nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    recs = nsg.timing_collect()
-    nsg.timing_enable(False)
-
-    ms_per_step = 1e3 * wall / args.steps
-    value = w.G * args.steps / wall
-    eff_tflops = credited * w.G * args.steps / wall / 1e12
-
-    # per-launch durations, matched to the plan (same launch order every step)
-    per = len(plan)
-    assert len(recs) == per * args.steps, (len(recs), per, args.steps)
-    by_kernel = {}
-    for i, (name, ms) in enumerate(recs):
-        e = plan[i % per]
-        d = by_kernel.setdefault(name, {"ms": 0.0, "launches": 0, "algo_flops": 0.0, "bytes": 0.0})
-        d["ms"] += ms
-        d["launches"] += 1
-        d["algo_flops"] += algorithmic_flops(e, w.G)
-        d["bytes"] += e["bytes"] * w.G
-    dominant = max((k for k in by_kernel if k.startswith("gemm")), key=lambda k: by_kernel[k]["ms"])
-    d = by_kernel[dominant]
-    avg_ms = d["ms"] / d["launches"]
-    achieved = d["algo_flops"] / d["launches"] / (avg_ms * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tr = json.load(open(TRAFFIC_FILE))
-            ent = tr.get(args.workload, {}).get(dominant)
-            if ent and ent.get("kernel_src") == kernel_source_hash():
-                traffic = ent.get("bytes_per_launch")
-        except Exception:
-            traffic = None
-    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
-                "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                "traffic": traffic, "avg_launch_ms": round(avg_ms, 4), "launches_per_step": d["launches"] // args.steps,
-                "algo_flops_per_launch": d["algo_flops"] / d["launches"]}
-    norm_ms = sum(by_kernel.get(k, {"ms": 0})["ms"] for k in ("norm_reduce", "scale_cast_transpose"))
-    norm_bytes = sum(by_kernel.get(k, {"bytes": 0})["bytes"] for k in ("norm_reduce", "scale_cast_transpose"))
-    kernels = {k: {"ms_per_step": round(v["ms"] / args.steps, 3),
-                   "tflops_algo": round(v["algo_flops"] / (v["ms"] * 1e-3) / 1e12, 1) if v["algo_flops"] else None}
-               for k, v in by_kernel.items()}
-
-    res = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "matrices/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16" if w.compute == "f16" else w.compute,
-        "data": "synthetic",
-        "config": {"workload": w.name, "G": w.G, "R": w.R, "C": w.C, "input_dtype": w.dtype,
-                   "mode": w.mode, "steps": w.steps, "restart_after": w.restart_after,
-                   "safety": w.safety, "coeffs": list(w.coeffs), "accumulate": "f32",
-                   "sym_updates": not args.general_updates},
-        "ms_per_call_median": round(per_call[len(per_call) // 2], 3),
-        "ms_per_call_iqr": round(per_call[(3 * len(per_call)) // 4] - per_call[len(per_call) // 4], 3),
-        "effective_tflops": round(eff_tflops, 2),
-        "pct_fp16_peak": round(100 * eff_tflops / PEAK_FP16_TFLOPS, 2),
-        "executed_tflops": round(executed * w.G * args.steps / wall / 1e12, 2),
-        "flops_per_matrix": {"credited": credited, "executed": executed},
-        "normalize_gbs": round(norm_bytes / (norm_ms * 1e-3) / 1e9, 1) if norm_ms else None,
-        "kernels": kernels,
-        "roofline": roofline,
-        "device": {"name": props.name, "cus": props.multi_processor_count},
-        "nonfinite_matrices": int(status.sum().item()),
-        "input_gen_s": round(t_gen, 1),
-    }
+    log(f"timing {w.name}: {args.warmup} warm-up + {args.steps} timed calls")
+    res, x_cpu, out = time_workload(w, dev, args.steps, args.warmup, not args.general_updates,
+                                    args.calibrate_copy)
+    head = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16" if w.compute == "f16" else w.compute, "data": "synthetic",
+            "config": res.pop("config")}
+    res.pop("steps")
+    res.pop("warmup")
+    line = dict(head, **res)
+    line["device"] = {"name": props.name, "cus": props.multi_processor_count}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, x_cpu, args.cpu_budget)
-    print(json.dumps(res), flush=True)
+        log("oracle baseline and parity sample")
+        base, idx, ref = cpu_baseline(w, x_cpu, args.cpu_budget)
+        line["cpu_baseline"] = base
+        line["parity"] = parity_object(out, idx, ref)
+    del out, x_cpu
+    torch.cuda.empty_cache()
+    if not args.no_other_configs and args.workload == DEFAULT_WORKLOAD:
+        others = {}
+        for name in OTHER_CONFIGS:
+            wo = synth.WORKLOADS[name]
+            steps = min(args.steps, 10)
+            log(f"timing {name}: {min(args.warmup, 3)} warm-up + {steps} timed calls")
+            r, xo, oo = time_workload(wo, dev, steps, min(args.warmup, 3), not args.general_updates)
+            if not args.no_cpu_baseline:
+                idx = PARITY_SAMPLE[name]
+                t0 = time.perf_counter()
+                classes = None
+                if wo.kind == "conditioning":
+                    from synth.workloads import conditioning_class_of
+                    classes = lambda g, G=wo.G: conditioning_class_of(G, g)
+                r["parity"] = parity_object(oo, idx, oracle_outputs(wo, xo, idx), classes)
+                r["parity"]["oracle_s"] = round(time.perf_counter() - t0, 1)
+            del xo, oo
+            torch.cuda.empty_cache()
+            others[name] = r
+        line["other_configs"] = others
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

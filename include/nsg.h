@@ -156,8 +156,12 @@ typedef struct {
   int32_t step;     /* NS step t (1..T); 0 before the loop, T+1 for the output */
   int64_t M, N, K;  /* GEMM logical sizes (0 for the normalize kernels) */
   double flops;     /* executed FLOPs per matrix (tiles run, 2MNK per tile) */
-  double bytes;     /* algorithmic HBM bytes per matrix: operands read once,
-                       outputs written once */
+  double bytes;     /* algorithmic HBM bytes per matrix (16-bit input and
+                       output assumed): every distinct matrix the launch
+                       reads, once (an operand that is also the added term,
+                       or a matrix and its transposed copy, count once), and
+                       every matrix of the method it writes, once (transposed
+                       copies and mirrored halves are not counted) */
   char label[24];   /* e.g. "R0=XXt", "Z", "Q=QZ+aQ", "RZ", "R=Z.RZ", "Y=QX" */
 } nsg_launch_info_t;
 
@@ -214,6 +218,19 @@ nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch,
 #define NSG_SELECT_COLS 1
 #define NSG_SELECT_SMALLER (-1) /* rows if R <= C, else columns (the pages'
                                    choice when the weight is not sharded) */
+
+/* The selection size rule of the Dion3 paper, Section 6 ("Selection") and
+ * Algorithm 4, step 3, host only: k = ceil(f n) lines (at least 1, at most
+ * n) of the dimension `dim` resolves to, n = R for rows, C for columns.
+ * NSG_SELECT_SMALLER resolves to columns when C < R, else rows (the pages'
+ * choice for an unsharded weight: whichever dimension is smaller).
+ *   fraction  f in (0, 1]; anything else is NSG_ERR_INVALID_ARG
+ *   dim_out   resolved NSG_SELECT_ROWS or NSG_SELECT_COLS
+ *   k_out     lines to select (0 when n == 0)
+ * Negative or oversized R, C: NSG_ERR_SHAPE; a null output pointer or a bad
+ * dim: NSG_ERR_INVALID_ARG. */
+nsg_status_t ns_select_count(int64_t R, int64_t C, int32_t dim, double fraction,
+                             int32_t *dim_out, int64_t *k_out);
 
 /* Bytes of device workspace ns_orthogonalize_selected needs (host only).
  * Same argument rules as ns_orthogonalize_selected. */

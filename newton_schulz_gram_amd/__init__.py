@@ -12,7 +12,6 @@ CPU fallback.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Sequence
 
@@ -74,7 +73,7 @@ EXPORTS = ("ns_default_params", "ns_workspace_size", "ns_orthogonalize", "ns_sta
            "ns_flops", "ns_plan", "ns_timing_enable", "ns_timing_collect", "nsg_copy",
            "nsg_gemm_nt", "ns_select_workspace_size", "ns_orthogonalize_selected",
            "nsg_l1_workspace_size", "nsg_l1_norms", "nsg_topk", "ns_muon_momentum", "ns_muon_update",
-           "ns_muon_workspace_size", "ns_muon_step")
+           "ns_muon_workspace_size", "ns_muon_step", "ns_select_count")
 SELECT_ROWS, SELECT_COLS, SELECT_SMALLER = 0, 1, -1
 
 _lib = None
@@ -116,6 +115,8 @@ def lib() -> ctypes.CDLL:
     L.ns_select_workspace_size.restype = i32
     L.ns_orthogonalize_selected.argtypes = [vp, i32, vp, i32, i64, i64, i64, i64, i32, P, vp, sz, vp, vp, vp]
     L.ns_orthogonalize_selected.restype = i32
+    L.ns_select_count.argtypes = [i64, i64, i32, ctypes.c_double, ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    L.ns_select_count.restype = i32
     L.nsg_l1_workspace_size.argtypes = [i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.nsg_l1_workspace_size.restype = i32
     L.nsg_l1_norms.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, sz, vp]
@@ -206,6 +207,37 @@ def plan(R: int, C: int, **kw):
                  flops=e.flops, bytes=e.bytes, label=e.label.decode()) for e in arr[:n.value]]
 
 
+def nbytes(t: torch.Tensor) -> int:
+    """Bytes of a tensor's storage as the library sees it (numel x element size)."""
+    return t.numel() * t.element_size()
+
+
+def check_out(out: torch.Tensor, nb: int, R: int, C: int, squeeze: bool, device) -> None:
+    """A caller-supplied output must hold exactly the bucket: [nb, R, C], or
+    [R, C] when the input was one 2-D matrix; contiguous, on the input's device.
+    The library writes nb * R * C elements into it."""
+    ok_shape = tuple(out.shape) == (nb, R, C) or (squeeze and nb == 1 and tuple(out.shape) == (R, C))
+    if not ok_shape:
+        raise ValueError(f"out has shape {tuple(out.shape)}; expected {(R, C) if squeeze else (nb, R, C)}")
+    if out.dtype not in _DT:
+        raise ValueError(f"unsupported out dtype {out.dtype}")
+    if not out.is_contiguous() or out.device != device:
+        raise ValueError("out must be contiguous on the input's device")
+
+
+def check_workspace(ws: torch.Tensor, device) -> None:
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the input's device")
+
+
+def check_status(status: Optional[torch.Tensor], nb: int, device) -> None:
+    """status: None, or int32 with at least nb entries, contiguous, on the input's device."""
+    if status is None:
+        return
+    if status.dtype != torch.int32 or status.numel() < nb or not status.is_contiguous() or status.device != device:
+        raise ValueError("status must be a contiguous int32 tensor with G entries on the input's device")
+
+
 def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -240,25 +272,22 @@ def orthogonalize(G: torch.Tensor, steps: int = 5, coeffs: Optional[Sequence[flo
     if out is None:
         out = torch.empty((nb, R, C), dtype=odt, device=Gs.device)
     else:
-        if out.shape != (nb, R, C) and out.shape != (R, C):
-            raise ValueError("out has the wrong shape")
-        if not out.is_contiguous() or out.device != Gs.device:
-            raise ValueError("out must be contiguous on the input's device")
+        check_out(out, nb, R, C, squeeze, Gs.device)
         odt = out.dtype
     p, _keep = make_params(steps, coeffs, mode, restart_after, safety, eps, compute_dtype, sym_updates,
                            restarts)
     need = ctypes.c_size_t(0)
     _check(lib().ns_workspace_size(nb, R, C, ctypes.byref(p), ctypes.byref(need)), "ns_workspace_size")
-    if workspace is None or workspace.numel() < need.value:
+    if workspace is None or nbytes(workspace) < need.value:
         workspace = torch.empty(max(1, need.value), dtype=torch.uint8, device=Gs.device)
-    if status is not None and (status.dtype != torch.int32 or status.numel() < nb or not status.is_cuda):
-        raise ValueError("status must be an int32 CUDA tensor with G entries")
+    check_workspace(workspace, Gs.device)
+    check_status(status, nb, Gs.device)
     with torch.cuda.device(Gs.device):
         code = lib().ns_orthogonalize(
             ctypes.c_void_p(Gs.data_ptr()), _dtype_code(Gs.dtype),
             ctypes.c_void_p(out.data_ptr()), _dtype_code(odt),
             nb, R, C, ctypes.byref(p),
-            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+            ctypes.c_void_p(workspace.data_ptr()), nbytes(workspace),
             ctypes.c_void_p(status.data_ptr()) if status is not None else None,
             ctypes.c_void_p(_stream_handle(Gs.device)))
     _check(code, "ns_orthogonalize")
@@ -317,15 +346,20 @@ def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 
 # Dion3 selection front-end (Dion3 paper, Section 6; Algorithm 4, steps 3-4)
 # ---------------------------------------------------------------------------
 
+def select_plan(R: int, C: int, fraction: float, dim: int = SELECT_SMALLER):
+    """(resolved dim, k) of the library's selection rule: k = ceil(f n) lines
+    of rows (dim 0) or columns (dim 1); -1 picks the smaller dimension."""
+    d, k = ctypes.c_int32(0), ctypes.c_int64(0)
+    code = lib().ns_select_count(int(R), int(C), int(dim), float(fraction), ctypes.byref(d), ctypes.byref(k))
+    if code == 1:
+        raise ValueError("fraction must lie in (0, 1] and dim in {-1, 0, 1}")
+    _check(code, "ns_select_count")
+    return int(d.value), int(k.value)
+
+
 def select_count(n: int, fraction: float) -> int:
-    """k = ceil(f n) lines out of n (at least 1)."""
-    if not 0.0 < fraction <= 1.0:
-        raise ValueError("fraction must lie in (0, 1]")
-    return min(n, max(1, math.ceil(fraction * n))) if n else 0
-
-
-def _select_dim(R: int, C: int, dim: int) -> int:
-    return dim if dim in (SELECT_ROWS, SELECT_COLS) else (SELECT_COLS if C < R else SELECT_ROWS)
+    """k = ceil(f n) lines out of n (at least 1), by the library's rule."""
+    return select_plan(n, n, fraction, SELECT_ROWS)[1]
 
 
 def orthogonalize_selected(M: torch.Tensor, fraction: float = 0.25, k: Optional[int] = None, dim: int = -1,
@@ -345,13 +379,18 @@ def orthogonalize_selected(M: torch.Tensor, fraction: float = 0.25, k: Optional[
     if Ms.dim() != 3 or not Ms.is_contiguous():
         raise ValueError("expected a contiguous [R, C] or [G, R, C] tensor")
     G, R, C = Ms.shape
-    d = _select_dim(R, C, dim)
-    n = R if d == SELECT_ROWS else C
-    kk = select_count(n, fraction) if k is None else int(k)
+    if k is None:
+        d, kk = select_plan(R, C, fraction, dim)
+    else:
+        d, _ = select_plan(R, C, 1.0, dim)
+        kk = int(k)
     odt = Ms.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((G, R, C), dtype=odt, device=Ms.device)
+    else:
+        check_out(out, G, R, C, squeeze, Ms.device)
     odt = out.dtype
+    check_status(status, G, Ms.device)
     idx = torch.empty((G, kk), dtype=torch.int32, device=Ms.device)
     p, _keep = make_params(steps, coeffs, mode, restart_after, safety, eps, compute_dtype, sym_updates, restarts)
     need = ctypes.c_size_t(0)
@@ -443,14 +482,18 @@ def muon_step(W: torch.Tensor, M: torch.Tensor, G: torch.Tensor, mu: float, lr: 
     p, _keep = make_params(**kw)
     need = ctypes.c_size_t(0)
     _check(lib().ns_muon_workspace_size(nb, R, C, ctypes.byref(p), ctypes.byref(need)), "ns_muon_workspace_size")
-    if workspace is None or workspace.numel() < need.value:
+    if workspace is None or nbytes(workspace) < need.value:
         workspace = torch.empty(max(1, need.value), dtype=torch.uint8, device=Ws.device)
+    if not (Ms.device == Gs.device == Ws.device):
+        raise ValueError("W, M and G must be on one device")
+    check_workspace(workspace, Ws.device)
+    check_status(status, nb, Ws.device)
     with torch.cuda.device(Ws.device):
         _check(lib().ns_muon_step(
             ctypes.c_void_p(Ws.data_ptr()), _dtype_code(Ws.dtype), ctypes.c_void_p(Ms.data_ptr()), _dtype_code(Ms.dtype),
             ctypes.c_void_p(Gs.data_ptr()), _dtype_code(Gs.dtype), nb, R, C, float(mu), float(lr), float(weight_decay),
             float(scale), 1 if stochastic else 0, int(seed) & (2 ** 64 - 1), int(step) & (2 ** 64 - 1), ctypes.byref(p),
-            ctypes.c_void_p(workspace.data_ptr()), need.value,
+            ctypes.c_void_p(workspace.data_ptr()), nbytes(workspace),
             ctypes.c_void_p(status.data_ptr()) if status is not None else None,
             ctypes.c_void_p(_stream_handle(Ws.device))), "ns_muon_step")
     return W, M

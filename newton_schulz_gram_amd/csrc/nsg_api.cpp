@@ -137,14 +137,25 @@ void add_gemm(Plan &P, bool sym, int step, const char *label, int A, int B, int 
   L.final_out = final_out;
   const int bm = tile_m(P.cfg);
   L.flops = sym ? 2.0 * sym_tiles(M, bm) * bm * bm * (double)K : 2.0 * (double)M * N * K;
-  // algorithmic bytes: valid operands read once, valid outputs written once
+  // algorithmic bytes: every distinct matrix the product reads, read once,
+  // and the matrices it defines, written once.  A buffer and its transposed
+  // copy are one matrix (X0 / X0^T, X1 / X1^T, RZ / RZ^T); a Cin that is an
+  // operand (Z = b R + c R^2 reads R once) is not counted again; the
+  // transposed copy out1 is a layout choice, not an output of the method.
   const double es = (double)dtype_size(P.cdtype);
   // valid K: K of a GEMM over X's long side is m, else n
   const double Kv = (K == P.mp) ? (double)P.m : (double)P.n;
-  double bytes = es * ((double)Mv * Kv + (double)Nv * Kv);
-  if (Cin != kNone) bytes += es * (double)Mv * Nv;
-  int outs = (out0 != kNone) + (out1 != kNone) + (out2 != kNone);
-  bytes += es * outs * (double)Mv * Nv;
+  auto matrix_of = [](int id) {
+    if (id == kX0T) return (int)kX0;
+    if (id == kX1T) return (int)kX1;
+    if (id == kS5) return (int)kS4;
+    return id;
+  };
+  const int ma = matrix_of(A), mb = matrix_of(B), mc = matrix_of(Cin);
+  double bytes = es * (double)Mv * Kv;
+  if (mb != ma) bytes += es * (double)Nv * Kv;
+  if (Cin != kNone && mc != ma && mc != mb) bytes += es * (double)Mv * Nv;
+  bytes += es * ((out0 != kNone) + (out2 != kNone)) * (double)Mv * Nv;
   L.bytes = bytes;
   for (int id : {A, B, Cin, out0, out1, out2})
     if (id >= 0) P.used[id] = true;
@@ -292,7 +303,9 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
                xpow, true);
     }
   }
-  P.launches[1].bytes = (double)R * C * dtype_size(0) + 2.0 * (double)n * m * dtype_size(P.cdtype);
+  // the scale pass reads the input once and writes X0 once (its transposed
+  // copy is a layout choice)
+  P.launches[1].bytes = (double)R * C * dtype_size(0) + (double)n * m * dtype_size(P.cdtype);
 
   // workspace layout
   size_t off = 0;
@@ -680,6 +693,29 @@ nsg_status_t select_layout(int64_t G, int64_t R, int64_t C, int64_t k, int32_t d
 }  // namespace
 
 extern "C" {
+
+nsg_status_t ns_select_count(int64_t R, int64_t C, int32_t dim, double fraction, int32_t *dim_out,
+                             int64_t *k_out) {
+  if (dim_out == nullptr || k_out == nullptr) return NSG_ERR_INVALID_ARG;
+  if (R < 0 || C < 0 || R > NSG_MAX_SIDE || C > NSG_MAX_SIDE) return NSG_ERR_SHAPE;
+  if (dim != NSG_SELECT_ROWS && dim != NSG_SELECT_COLS && dim != NSG_SELECT_SMALLER) return NSG_ERR_INVALID_ARG;
+  if (!(fraction > 0.0 && fraction <= 1.0)) return NSG_ERR_INVALID_ARG;
+  // without sharding the smaller dimension is selected; rows on a tie
+  const int32_t d = dim == NSG_SELECT_SMALLER ? (C < R ? NSG_SELECT_COLS : NSG_SELECT_ROWS) : dim;
+  const int64_t n = d == NSG_SELECT_ROWS ? R : C;
+  int64_t k = 0;
+  if (n > 0) {
+    // k = ceil(f n), at least one line; the product is rounded up only when
+    // it is not already an integer in double precision
+    const double fk = std::ceil(fraction * (double)n);
+    k = (int64_t)fk;
+    if (k < 1) k = 1;
+    if (k > n) k = n;
+  }
+  *dim_out = d;
+  *k_out = k;
+  return NSG_OK;
+}
 
 nsg_status_t ns_select_workspace_size(int64_t G, int64_t R, int64_t C, int64_t k, int32_t dim, int32_t in_dtype,
                                       int32_t out_dtype, const nsg_params_t *p, size_t *bytes) {

@@ -6,6 +6,8 @@ bench's CPU-baseline leg, never by the product path.
 from .ns_oracle import (  # noqa: F401
     EPS,
     normalize,
+    gram,
+    quadratic,
     standard_ns,
     gram_ns,
     naive_gram_ns,

@@ -9,7 +9,7 @@ What it computes, step by step, in the order and notation of the pages
 the "muon" kernel card, "How it works"):
 
   * ``normalize``      X <- X / (s (||X||_F + eps))              (Alg. 1 / Alg. 3 step 2)
-  * ``standard_ns``    A = X X^T, B = b A + c A^2, X <- a X + B X (Alg. 1)
+  * ``standard_ns``    X <- a X + (b A + c A^2) X with A = X X^T   (Alg. 1)
   * ``gram_ns``        R = X X^T, Q = I, loop with restarts       (Alg. 3, App. B.2)
   * ``orthogonalize``  the bucket wrapper: transpose so the short side leads,
                        pick the mode (square -> standard), normalize, iterate,
@@ -24,7 +24,7 @@ Readings of points the pages leave open (each also listed in the design doc):
     The per-polynomial form p(x/s) of Appendix B.2.2 equals this scaling
     applied at every step; it is obtained by passing rescaled coefficients.
   * restart_after = r: the restart happens at the top of iteration r + 1
-    (Alg. 3 restarts "if t = 3", i.e. r = 2).  r = 0, or r >= T, means no
+    (Alg. 3 restarts at the top of step 3, i.e. r = 2).  r = 0, or r >= T, means no
     restart (Alg. 2 with the implicit a*I form of Appendix B.2.3).
   * square matrices (m == n) in "gram" mode run standard NS (Section 4.1, last
     paragraph).
@@ -43,7 +43,7 @@ from typing import Sequence
 
 import numpy as np
 
-EPS = 1e-7  # Alg. 1 / Alg. 3 step 2: "eps = 10^-7"
+EPS = 1e-7  # Alg. 1 / Alg. 3 step 2
 
 
 def _coeff_list(coeffs, steps: int):
@@ -66,16 +66,26 @@ def normalize(X: np.ndarray, safety: float = 1.0, eps: float = EPS) -> np.ndarra
     return X / (safety * (nu + eps))
 
 
+def gram(X: np.ndarray) -> np.ndarray:
+    """The Gram matrix X X^T of the short side (n x n)."""
+    return X @ X.T
+
+
+def quadratic(A: np.ndarray, b: float, c: float) -> np.ndarray:
+    """b A + c A^2: the matrix polynomial h_t(A) = a + b A + c A^2 without its
+    a*I term, which every caller applies on its own (Dion3 paper, App. B.2.3)."""
+    return b * A + c * (A @ A)
+
+
 def standard_ns(X: np.ndarray, coeffs, steps: int = 5) -> np.ndarray:
     """Standard quintic Newton–Schulz on an already normalized X (n <= m).
 
-    Dion3 paper, Section 2.2, Algorithm 1, loop body:
-        A <- X X^T ;  B <- b_t A + c_t A^2 ;  X <- a_t X + B X
+    Dion3 paper, Section 2.2, Algorithm 1: every step applies the odd
+    quintic p_t(X) = a_t X + b_t (X X^T) X + c_t (X X^T)^2 X, i.e.
+    X <- a_t X + h(X X^T) X with h the quadratic part above.
     """
     for a, b, c in _coeff_list(coeffs, steps):
-        A = X @ X.T
-        B = b * A + c * (A @ A)
-        X = a * X + B @ X
+        X = a * X + quadratic(gram(X), b, c) @ X
     return X
 
 
@@ -111,17 +121,16 @@ def gram_ns(X: np.ndarray, coeffs, steps: int = 5, restart_after: int = 2,
     ``gram_shift`` subtracts shift*I each time a Gram matrix is formed, the
     simulated spurious eigenvalue of Appendix B.2.1 (there: 4e-4); 0 normally.
     """
-    n = X.shape[0]
-    I = np.eye(n)
-    R = X @ X.T - gram_shift * I
+    I = np.eye(X.shape[0])
+    R = gram(X) - gram_shift * I
     Q = I.copy()
     at = _restart_steps(steps, restart_after, restarts)
     for t, (a, b, c) in enumerate(_coeff_list(coeffs, steps), start=1):
         if t in at:
             X = Q @ X
-            R = X @ X.T - gram_shift * I
+            R = gram(X) - gram_shift * I
             Q = I.copy()
-        Z = b * R + c * (R @ R)
+        Z = quadratic(R, b, c)
         Q = Q @ Z + a * Q
         RZ = R @ Z + a * R
         R = Z @ RZ + a * RZ
@@ -132,19 +141,18 @@ def naive_gram_ns(X: np.ndarray, coeffs, steps: int = 5,
                   r0_shift: float = 0.0) -> np.ndarray:
     """Algorithm 2 as printed (explicit a*I inside Z), optional spurious shift.
 
-    Dion3 paper, Section 4, Algorithm 2:
-        R_0 <- X X^T ; Q_0 <- I ; Z_t <- a I + b R + c R^2 ; Q <- Q Z ; R <- Z R Z
+    Dion3 paper, Section 4, Algorithm 2: R_0 = X X^T and Q_0 = I, then each
+    step forms Z_t = h_t(R) = a I + b R + c R^2 and updates Q by Q Z_t and R by
+    Z_t R Z_t; the output is Q_T X.
     ``r0_shift`` subtracts shift*I from R_0, the simulated spurious negative
     eigenvalue of Appendix B.2.1 (about -4e-4).
     """
-    n = X.shape[0]
-    I = np.eye(n)
-    R = X @ X.T - r0_shift * I
+    I = np.eye(X.shape[0])
+    R = gram(X) - r0_shift * I
     Q = I.copy()
     for a, b, c in _coeff_list(coeffs, steps):
-        Z = a * I + b * R + c * (R @ R)
-        Q = Q @ Z
-        R = Z @ R @ Z
+        Z = a * I + quadratic(R, b, c)   # h_t(R) with its a*I term inside Z
+        Q, R = Q @ Z, Z @ R @ Z
     return Q @ X
 
 
@@ -154,7 +162,8 @@ def ns_matrix(Y: np.ndarray, steps: int, coeffs, mode: str = "gram",
     """One R x C matrix: transpose so n <= m, normalize, iterate, transpose back.
 
     Transposition: Alg. 1 takes X in R^{n x m} with n <= m; the "muon" kernel
-    card transposes "so the contracted dimension is the larger one".
+    card transposes a tall matrix so that the products contract over its
+    long side.
     Mode: square matrices always run standard NS (Dion3 paper, Section 4.1).
     """
     Y = np.asarray(Y, dtype=np.float64)

@@ -1,9 +1,19 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
-Bars: relative Frobenius error <= 3e-2 and cosine >= 0.97 per matrix for the
-fp16/bf16 paths, <= 1e-4 for the fp32 debug path; grouped and single-matrix
-outputs bitwise identical; repeated calls bitwise identical.
+Bars per matrix (tests/parity_metrics.py defines the measures):
+  * relative Frobenius error <= 3e-2 and cosine >= 0.97 for the fp16/bf16
+    paths, relative error <= 1e-4 for the fp32 debug path (the pages' bars);
+  * on the full-size buckets also a worst 256 x 256 block error and a worst
+    single-element error, both against the matrix's RMS entry: a wrong tile,
+    or a corner of one, fails these while it barely moves the whole-matrix
+    norm.  Their bars are fixed multiples of the errors these kernels show on
+    the same seeded inputs (recorded with the bars below);
+  * grouped and single-matrix outputs bitwise identical; repeated calls
+    bitwise identical.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -11,12 +21,20 @@ import torch
 import newton_schulz_gram_amd as nsg
 import oracle
 import synth
+from parity_metrics import bucket_errors, summary
 from synth import COEFFS_MUON, WORKLOADS
 from synth.workloads import conditioning_class_of, custom
 
 pytestmark = pytest.mark.gpu
 
 HALF_REL, HALF_COS, F32_REL = 3e-2, 0.97, 1e-4
+
+# Localized bars for the full-size buckets: worst 256 x 256 block RMS error and
+# worst element error, both divided by the matrix's RMS entry.
+BLOCK_BAR = {"gaussian": 1e-2, "ill_conditioned": 6e-2, "low_rank": 8e-2, "heavy_tailed": 1e-2,
+             "scaled_up": 1e-2, "scaled_down": 1e-2, "near_orthogonal": 1e-2}
+ELEM_BAR = {"gaussian": 5e-2, "ill_conditioned": 0.4, "low_rank": 0.5, "heavy_tailed": 5e-2,
+            "scaled_up": 5e-2, "scaled_down": 5e-2, "near_orthogonal": 5e-2}
 
 
 def metrics(out, ref):
@@ -49,6 +67,30 @@ def check(out, ref, compute, label=""):
         assert rel.max() <= HALF_REL, (label, rel.max(), int(rel.argmax()))
         assert cos.min() >= HALF_COS, (label, cos.min())
     return rel, cos
+
+
+def record(label, stats):
+    """Print one line of measured errors (and keep it under gpurun_out/ when
+    that folder exists, for the design notes)."""
+    line = json.dumps({"case": label, **{k: (round(v, 7) if isinstance(v, float) else v)
+                                         for k, v in stats.items()}})
+    print(line, flush=True)
+    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+    if os.path.isdir(d):
+        with open(os.path.join(d, "parity_errors.jsonl"), "a") as fh:
+            fh.write(line + "\n")
+
+
+def check_local(out, ref, label, cls="gaussian"):
+    """Every bar on every matrix: rel / cos, worst block, worst element."""
+    errs = bucket_errors(out, ref)
+    s = summary(errs)
+    record(label, s)
+    assert s["rel_max"] <= HALF_REL, (label, s)
+    assert s["cos_min"] >= HALF_COS, (label, s)
+    assert s["block_rel_max"] <= BLOCK_BAR[cls], (label, s)
+    assert s["elem_max"] <= ELEM_BAR[cls], (label, s)
+    return errs
 
 
 # ---------------------------------------------------------------------------
@@ -117,19 +159,25 @@ def test_per_step_coefficients_and_steps():
 # GPT-2-small MLP bucket: 42 x 768x3072, seven conditionings
 # ---------------------------------------------------------------------------
 
+def per_class(w, out, ref, label):
+    """Bars per conditioning class (every matrix of the class)."""
+    o = out.double().cpu().numpy()
+    by = {}
+    for g in range(w.G):
+        by.setdefault(conditioning_class_of(w.G, g), []).append(g)
+    worst = {}
+    for cls, idx in by.items():
+        worst[cls] = check_local(o[idx], ref[idx], f"{label}/{cls}", cls)
+    return {c: max(e["rel"] for e in v) for c, v in worst.items()}
+
+
 def test_gpt2s_bucket_all_conditionings():
     w = WORKLOADS["gpt2s_mlp_42x768x3072_f16"]
     x = synth.make(w)
     ref = oracle_of(x, safety=w.safety)
     out = run(x, safety=w.safety)
-    rel, cos = metrics(out, ref)
-    worst = {}
-    for g in range(w.G):
-        c = conditioning_class_of(w.G, g)
-        worst[c] = max(worst.get(c, 0.0), float(rel[g]))
+    worst = per_class(w, out, ref, "gpt2s")
     print("per-class max rel error:", {k: round(v, 5) for k, v in worst.items()})
-    assert rel.max() <= HALF_REL, worst
-    assert cos.min() >= HALF_COS
     # grouped == single, bitwise
     for g in (0, 13, 41):
         one = run(x[g:g + 1], safety=w.safety)
@@ -137,6 +185,32 @@ def test_gpt2s_bucket_all_conditionings():
     # repeated call, bitwise
     again = run(x, safety=w.safety)
     assert torch.equal(again, out)
+
+
+def test_gpt2s_forced_symmetry_under_stress():
+    """Forced symmetry under the pages' stress setup (Dion3 paper, App. B.2.3:
+    restart after three steps instead of two, safety 1.02 instead of 1.05):
+    symmetric updates (Q Z + a Q and R Z + a R computed as lower triangles and
+    mirrored) against general updates, every conditioning class.  Both must
+    stay finite with a clear status flag and within the bars, and the
+    symmetric form may not be worse than the general one on any class by more
+    than a quarter (plus 1e-3 of slack for rounding order)."""
+    w = WORKLOADS["gpt2s_mlp_42x768x3072_f16"]
+    x = synth.make(w)
+    ref = oracle_of(x, restart_after=3, safety=1.02)
+    xc = x.cuda()
+    res = {}
+    for sym in (True, False):
+        st = torch.full((w.G,), 7, dtype=torch.int32, device="cuda")
+        out = nsg.orthogonalize(xc, restart_after=3, safety=1.02, sym_updates=sym, status=st)
+        torch.cuda.synchronize()
+        assert st.sum().item() == 0, st.tolist()
+        assert bool(torch.isfinite(out.float()).all())
+        res[sym] = per_class(w, out, ref, f"gpt2s_stress_r3_s1.02/{'sym' if sym else 'gen'}")
+    print("stress per-class max rel error (sym, gen):",
+          {c: (round(res[True][c], 5), round(res[False][c], 5)) for c in res[True]})
+    for c in res[True]:
+        assert res[True][c] <= 1.25 * res[False][c] + 1e-3, (c, res[True][c], res[False][c])
 
 
 # ---------------------------------------------------------------------------
@@ -147,16 +221,17 @@ def test_moe_bucket_sampled():
     w = WORKLOADS["moe_512x2048x512_f16"]
     x = synth.make(w)
     out = run(x, safety=w.safety)
-    idx = [0, 1, 77, 255, 300, 511]
+    idx = sorted(set(list(range(0, 512, 16)) + [1, 77, 255, 300, 511]))
     ref = oracle_of(x[idx], safety=w.safety)
-    check(out[idx], ref, "f16", "moe")
+    check_local(out[idx], ref, f"moe x{len(idx)}")
     for g in (0, 300):
         one = run(x[g:g + 1], safety=w.safety)
         assert torch.equal(one[0], out[g])
 
 
 # ---------------------------------------------------------------------------
-# Full-size buckets, sampled against the oracle
+# Full-size buckets, sampled against the oracle (four matrices each, every
+# element and every 256 x 256 block checked)
 # ---------------------------------------------------------------------------
 
 def test_llama7b_bucket_sampled():
@@ -164,20 +239,26 @@ def test_llama7b_bucket_sampled():
     x = synth.make(w)
     out = run(x, safety=w.safety)
     assert out.dtype == torch.bfloat16 and out.shape == (32, 11008, 4096)
-    ref = oracle_of(x[:1], safety=w.safety)
-    rel, cos = check(out[:1], ref, "f16", "7b")
-    print("7b matrix 0: rel %.3e cos %.6f" % (rel[0], cos[0]))
+    idx = [0, 11, 22, 31]
+    o = out[idx].cpu()
     one = run(x[5:6], safety=w.safety)
     assert torch.equal(one[0], out[5])
+    del out, one
+    ref = oracle_of(x[idx], safety=w.safety)
+    check_local(o, ref, "llama7b x4")
 
 
 def test_square_bucket_standard_fallback_sampled():
     w = WORKLOADS["square_32x4096x4096_f16"]
     x = synth.make(w)
     out = run(x, safety=w.safety)
-    ref = oracle_of(x[31:32], safety=w.safety)
-    rel, cos = check(out[31:32], ref, "f16", "square")
-    print("square matrix 31: rel %.3e cos %.6f" % (rel[0], cos[0]))
+    idx = [0, 10, 21, 31]
+    o = out[idx].cpu()
+    one = run(x[10:11], safety=w.safety)
+    assert torch.equal(one[0], out[10])
+    del out, one
+    ref = oracle_of(x[idx], safety=w.safety)
+    check_local(o, ref, "square x4")
 
 
 # ---------------------------------------------------------------------------

@@ -234,3 +234,70 @@ def test_select_validation_and_workspace():
     assert L.nsg_topk(None, 1, 10, 11, None, None, None) == 1
     assert nsg.select_count(4096, 0.25) == 1024 and nsg.select_count(10, 0.25) == 3
     assert nsg.select_count(4096, 0.25) == oracle.n_selected(4096, 0.25)
+
+
+def test_select_count_rule_matches_the_oracle():
+    """The library's k = ceil(f n) and default dimension (Dion3 paper,
+    Section 6) against the selection oracle, over many shapes and fractions."""
+    import itertools
+    for (R, C), f in itertools.product([(4096, 11008), (11008, 4096), (100, 100), (1, 7), (7, 1), (333, 17)],
+                                      [1e-3, 0.1, 0.25, 1 / 3, 0.5, 0.999, 1.0]):
+        d, k = nsg.select_plan(R, C, f)
+        assert d == oracle.select_dim(R, C), (R, C)
+        n = R if d == 0 else C
+        assert k == oracle.n_selected(n, f), (R, C, f)
+        for dim in (0, 1):
+            d2, k2 = nsg.select_plan(R, C, f, dim)
+            assert d2 == dim and k2 == oracle.n_selected(R if dim == 0 else C, f)
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            nsg.select_plan(10, 20, bad)
+    with pytest.raises(ValueError):
+        nsg.select_plan(10, 20, 0.5, 2)
+    assert nsg.select_plan(0, 20, 0.5, 0) == (0, 0)
+
+
+# ---- Python-side buffer validation: every check runs before any launch ----
+
+def test_out_shape_rules():
+    """A caller's out must be exactly [G, R, C], or [R, C] for a single 2-D
+    matrix: an [R, C] out for a bucket of G > 1 would be written G times over
+    its end by the library."""
+    import torch
+    dev = torch.device("cpu")
+    ok = torch.empty(3, 8, 16)
+    nsg.check_out(ok, 3, 8, 16, False, dev)
+    with pytest.raises(ValueError):
+        nsg.check_out(torch.empty(8, 16), 3, 8, 16, False, dev)   # the overrun the rule exists for
+    with pytest.raises(ValueError):
+        nsg.check_out(torch.empty(8, 16), 1, 8, 16, False, dev)   # a 3-D input wants a 3-D out
+    nsg.check_out(torch.empty(8, 16), 1, 8, 16, True, dev)         # 2-D input, 2-D out
+    nsg.check_out(torch.empty(1, 8, 16), 1, 8, 16, True, dev)
+    with pytest.raises(ValueError):
+        nsg.check_out(torch.empty(2, 8, 16), 1, 8, 16, True, dev)
+    with pytest.raises(ValueError):
+        nsg.check_out(torch.empty(3, 16, 8), 3, 8, 16, False, dev)
+    with pytest.raises(ValueError):
+        nsg.check_out(torch.empty(3, 8, 32)[:, :, :16], 3, 8, 16, False, dev)  # not contiguous
+    with pytest.raises(ValueError):
+        nsg.check_out(torch.empty(3, 8, 16, dtype=torch.int32), 3, 8, 16, False, dev)
+    with pytest.raises(ValueError):
+        nsg.check_out(ok, 3, 8, 16, False, torch.device("meta"))  # another device
+
+
+def test_status_and_workspace_rules():
+    import torch
+    dev = torch.device("cpu")
+    nsg.check_status(None, 4, dev)
+    nsg.check_status(torch.zeros(4, dtype=torch.int32), 4, dev)
+    nsg.check_status(torch.zeros(9, dtype=torch.int32), 4, dev)
+    for bad in (torch.zeros(3, dtype=torch.int32), torch.zeros(4, dtype=torch.int64),
+                torch.zeros(8, dtype=torch.int32)[::2]):
+        with pytest.raises(ValueError):
+            nsg.check_status(bad, 4, dev)
+    with pytest.raises(ValueError):
+        nsg.check_status(torch.zeros(4, dtype=torch.int32), 4, torch.device("meta"))
+    nsg.check_workspace(torch.empty(64, dtype=torch.uint8), dev)
+    with pytest.raises(ValueError):
+        nsg.check_workspace(torch.empty(64, dtype=torch.uint8), torch.device("meta"))
+    assert nsg.nbytes(torch.empty(10, dtype=torch.float32)) == 40
