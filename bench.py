@@ -432,7 +432,11 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
             traffic = None
     common = {"kernel": dominant, "traffic": traffic, "avg_launch_ms": round(avg_ms, 4),
               "launches_per_step": d["launches"] // steps}
-    if bound == "hbm":
+    if bound == "latency":
+        roofline = {"bound": "latency", "achieved": None, "peak": None, "unit": None, "frac": None,
+                    "us_per_launch": round(1e3 * sum(v["ms"] for v in by_kernel.values()) / len(recs), 2),
+                    "launches_per_step": per, **{k: common[k] for k in ("kernel", "avg_launch_ms")}}
+    elif bound == "hbm":
         achieved = d["bytes"] / d["launches"] / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4), **common,
