@@ -56,7 +56,9 @@ typedef enum {
   NSG_ERR_UNSUPPORTED_DTYPE = 2,   /* dtype code outside nsg_dtype_t */
   NSG_ERR_SHAPE = 3,               /* negative size, or a side above NSG_MAX_SIDE */
   NSG_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace null, misaligned or too small */
-  NSG_ERR_HIP = 5                  /* a HIP runtime call or kernel launch failed */
+  NSG_ERR_HIP = 5,                 /* a HIP runtime call or kernel launch failed */
+  NSG_ERR_SCRATCH_TOO_SMALL = 6    /* ns_orthogonalize_noalloc: the bucket's workspace
+                                      exceeds NSG_NOALLOC_MAX_BYTES */
 } nsg_status_t;
 
 typedef enum { NSG_F16 = 0, NSG_BF16 = 1, NSG_F32 = 2 } nsg_dtype_t;
@@ -132,6 +134,30 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype,
                               const nsg_params_t *p,
                               void *workspace, size_t workspace_bytes,
                               int32_t *status, void *stream);
+
+/* ns_orthogonalize without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing and calls no
+ * allocating routine.  Its workspace is a fixed array of
+ * NSG_NOALLOC_MAX_BYTES inside the library: one copy per GPU, held from the
+ * library's first use of that GPU until the process ends.
+ *   in, out, G, R, C, p, status, stream: as for ns_orthogonalize (in, out and
+ *           status are the caller's device memory).
+ * A bucket whose ns_workspace_size exceeds NSG_NOALLOC_MAX_BYTES returns
+ * NSG_ERR_SCRATCH_TOO_SMALL before anything is enqueued; other argument
+ * errors as for ns_orthogonalize.  The array is looked up on the device
+ * current on the calling thread, which must be the device of `stream`.
+ * Every call on one GPU uses that GPU's single array: two calls that may
+ * overlap on one GPU (different streams, or different host threads without
+ * stream ordering between them) race on it.  Calls ordered on one stream are
+ * safe; no call depends on what an earlier call left in the array.
+ * Results are bit for bit those of ns_orthogonalize. */
+#define NSG_NOALLOC_MAX_BYTES (128u << 20) /* 128 MiB */
+nsg_status_t ns_orthogonalize_noalloc(const void *in, int32_t in_dtype,
+                                      void *out, int32_t out_dtype,
+                                      int64_t G, int64_t R, int64_t C,
+                                      const nsg_params_t *p, int32_t *status,
+                                      void *stream);
 
 /* Static text for a status code. */
 const char *ns_status_string(nsg_status_t s);

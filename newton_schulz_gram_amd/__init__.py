@@ -32,7 +32,9 @@ _MODES = {"standard": NSG_STANDARD, "gram": NSG_GRAM}
 KIND_NAMES = {0: "norm_reduce", 1: "scale_cast_transpose", 2: "gemm_nt", 3: "gemm_nt_sym"}
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype", 3: "unsupported shape",
-          4: "workspace missing, misaligned or too small", 5: "HIP runtime error"}
+          4: "workspace missing, misaligned or too small", 5: "HIP runtime error",
+          6: "bucket needs more than the fixed no-allocation scratch"}
+NOALLOC_MAX_BYTES = 128 << 20  # NSG_NOALLOC_MAX_BYTES
 
 
 class NSGError(RuntimeError):
@@ -73,7 +75,7 @@ EXPORTS = ("ns_default_params", "ns_workspace_size", "ns_orthogonalize", "ns_sta
            "ns_flops", "ns_plan", "ns_timing_enable", "ns_timing_collect", "nsg_copy",
            "nsg_gemm_nt", "ns_select_workspace_size", "ns_orthogonalize_selected",
            "nsg_l1_workspace_size", "nsg_l1_norms", "nsg_topk", "ns_muon_momentum", "ns_muon_update",
-           "ns_muon_workspace_size", "ns_muon_step", "ns_select_count")
+           "ns_muon_workspace_size", "ns_muon_step", "ns_select_count", "ns_orthogonalize_noalloc")
 SELECT_ROWS, SELECT_COLS, SELECT_SMALLER = 0, 1, -1
 
 _lib = None
@@ -96,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.ns_workspace_size.restype = i32
     L.ns_orthogonalize.argtypes = [vp, i32, vp, i32, i64, i64, i64, P, vp, sz, vp, vp]
     L.ns_orthogonalize.restype = i32
+    L.ns_orthogonalize_noalloc.argtypes = [vp, i32, vp, i32, i64, i64, i64, P, vp, vp]
+    L.ns_orthogonalize_noalloc.restype = i32
     L.ns_status_string.argtypes = [i32]
     L.ns_status_string.restype = ctypes.c_char_p
     L.ns_flops.argtypes = [i64, i64, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
@@ -292,6 +296,36 @@ def orthogonalize(G: torch.Tensor, steps: int = 5, coeffs: Optional[Sequence[flo
             ctypes.c_void_p(_stream_handle(Gs.device)))
     _check(code, "ns_orthogonalize")
     return out[0] if (squeeze and out.dim() == 3) else out
+
+
+def orthogonalize_noalloc(G: torch.Tensor, out: torch.Tensor, steps: int = 5,
+                          coeffs: Optional[Sequence[float]] = None, mode: str = "gram", restart_after: int = 2,
+                          safety: float = 1.05, eps: float = 1e-7, compute_dtype="f16",
+                          status: Optional[torch.Tensor] = None, sym_updates: bool = True,
+                          restarts: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """orthogonalize() through ns_orthogonalize_noalloc: the library's fixed
+    scratch array is the workspace, so neither the library nor this wrapper
+    allocates device memory (the caller passes `out`).  Buckets whose
+    workspace exceeds NOALLOC_MAX_BYTES raise NSGError (status 6).  Calls that
+    may overlap on one GPU share that scratch and race."""
+    if not G.is_cuda:
+        raise ValueError("orthogonalize_noalloc needs a GPU tensor (no CPU path)")
+    squeeze = G.dim() == 2
+    Gs = G.unsqueeze(0) if squeeze else G
+    if Gs.dim() != 3 or not Gs.is_contiguous():
+        raise ValueError("expected a contiguous [R, C] or [G, R, C] tensor")
+    nb, R, C = Gs.shape
+    check_out(out, nb, R, C, squeeze, Gs.device)
+    check_status(status, nb, Gs.device)
+    p, _keep = make_params(steps, coeffs, mode, restart_after, safety, eps, compute_dtype, sym_updates, restarts)
+    with torch.cuda.device(Gs.device):
+        code = lib().ns_orthogonalize_noalloc(
+            ctypes.c_void_p(Gs.data_ptr()), _dtype_code(Gs.dtype), ctypes.c_void_p(out.data_ptr()),
+            _dtype_code(out.dtype), nb, R, C, ctypes.byref(p),
+            ctypes.c_void_p(status.data_ptr()) if status is not None else None,
+            ctypes.c_void_p(_stream_handle(Gs.device)))
+    _check(code, "ns_orthogonalize_noalloc")
+    return out
 
 
 def timing_enable(on: bool = True):

@@ -350,6 +350,39 @@ hipEvent_t take_event() {
   return e;
 }
 
+// ---- fixed scratch for the entry point that allocates nothing ----
+// The workspace of ns_orthogonalize_noalloc: one array per GPU, held by the
+// library from its first use on that GPU until the process ends.  Host code
+// never passes `scratch` itself (in host code the name is a host-side
+// stand-in, not a device address): it uses the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+}  // namespace nsg
+
+static __device__ __align__(256) unsigned char scratch[NSG_NOALLOC_MAX_BYTES];
+
+namespace nsg {
+namespace {
+
+// Device address of this device's scratch array (the device current on the
+// calling thread), looked up on the first call per device.
+nsg_status_t scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NSG_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return NSG_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NSG_OK;
+}
+
 }  // namespace
 }  // namespace nsg
 
@@ -383,6 +416,7 @@ const char *ns_status_string(nsg_status_t s) {
     case NSG_ERR_SHAPE: return "unsupported shape";
     case NSG_ERR_WORKSPACE_TOO_SMALL: return "workspace missing, misaligned or too small";
     case NSG_ERR_HIP: return "HIP runtime error";
+    case NSG_ERR_SCRATCH_TOO_SMALL: return "bucket needs more than the fixed no-allocation scratch";
   }
   return "unknown status";
 }
@@ -563,6 +597,25 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
     }
   }
   return NSG_OK;
+}
+
+nsg_status_t ns_orthogonalize_noalloc(const void *in, int32_t in_dtype, void *out, int32_t out_dtype, int64_t G,
+                                      int64_t R, int64_t C, const nsg_params_t *p, int32_t *status, void *stream) {
+  size_t need = 0;
+  nsg_status_t st = ns_workspace_size(G, R, C, p, &need);
+  if (st != NSG_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
+  if (G == 0 || R == 0 || C == 0) return NSG_OK;
+  if (in == nullptr || out == nullptr) return NSG_ERR_INVALID_ARG;
+  if (need > (size_t)NSG_NOALLOC_MAX_BYTES) return NSG_ERR_SCRATCH_TOO_SMALL;
+  void *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != NSG_OK) return st;
+  // Every buffer the kernels read from the workspace is written first in
+  // the same call (partial sums, scales, X0 with its zero padding, every
+  // product with its padding), so the previous call's contents never matter.
+  return ns_orthogonalize(in, in_dtype, out, out_dtype, G, R, C, p, ws, (size_t)NSG_NOALLOC_MAX_BYTES, status,
+                          stream);
 }
 
 nsg_status_t ns_timing_enable(int32_t on) {

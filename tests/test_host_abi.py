@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = nsg.lib()
-    for code in range(6):
+    for code in range(7):
         assert L.ns_status_string(code).decode() == nsg.STATUS[code]
 
 
@@ -301,3 +301,24 @@ def test_status_and_workspace_rules():
     with pytest.raises(ValueError):
         nsg.check_workspace(torch.empty(64, dtype=torch.uint8), torch.device("meta"))
     assert nsg.nbytes(torch.empty(10, dtype=torch.float32)) == 40
+
+
+def test_noalloc_rejects_before_any_gpu_call():
+    """ns_orthogonalize_noalloc checks its arguments and the bucket's workspace
+    against its fixed scratch before it touches a device."""
+    L = nsg.lib()
+    p, keep = nsg.make_params()
+    fake_in, fake_out = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+    # the 7B bucket needs ~17 GB of workspace: more than the fixed scratch
+    assert nsg.workspace_size(32, 11008, 4096) > nsg.NOALLOC_MAX_BYTES
+    assert L.ns_orthogonalize_noalloc(fake_in, 1, fake_out, 1, 32, 11008, 4096, ctypes.byref(p), None, None) == 6
+    assert L.ns_status_string(6).decode() == nsg.STATUS[6]
+    # argument errors as for ns_orthogonalize
+    bad, keep2 = nsg.make_params(steps=0)
+    assert L.ns_orthogonalize_noalloc(fake_in, 0, fake_out, 0, 2, 64, 128, ctypes.byref(bad), None, None) == 1
+    assert L.ns_orthogonalize_noalloc(fake_in, 9, fake_out, 0, 2, 64, 128, ctypes.byref(p), None, None) == 2
+    assert L.ns_orthogonalize_noalloc(None, 0, fake_out, 0, 2, 64, 128, ctypes.byref(p), None, None) == 1
+    assert L.ns_orthogonalize_noalloc(fake_in, 0, fake_out, 0, -1, 64, 128, ctypes.byref(p), None, None) == 3
+    # an empty bucket is a no-op
+    assert L.ns_orthogonalize_noalloc(None, 0, None, 0, 0, 64, 128, ctypes.byref(p), None, None) == 0
+    assert "NSG_NOALLOC_MAX_BYTES (128u << 20)" in open(HEADER).read()
