@@ -189,6 +189,8 @@ typedef struct {
                        every matrix of the method it writes, once (transposed
                        copies and mirrored halves are not counted) */
   char label[24];   /* e.g. "R0=XXt", "Z", "Q=QZ+aQ", "RZ", "R=Z.RZ", "Y=QX" */
+  int32_t a_kmajor; /* 1: A is read from a K-major buffer (K x M), else M x K */
+  int32_t b_kmajor; /* 1: B is read from a K-major buffer (K x N), else N x K */
 } nsg_launch_info_t;
 
 /* Writes up to max_entries launch descriptions for one call on an R x C
@@ -220,6 +222,10 @@ nsg_status_t nsg_copy(const void *src, void *dst, size_t bytes, void *stream);
  *   out_t_b = V^T         (row-major N x M, ld ldt)       if out_t != NULL
  *   out_d_b = V + diag*I  (row-major M x N, ld ldo)       if out_d != NULL
  * A_b is M x K (ld lda), B_b is N x K (ld ldb), Cin_b is M x N (ld ldc);
+ * with a_trans = 1 A_b is stored K-major instead (K x M, ld lda >= M), with
+ * b_trans = 1 likewise B_b (K x N, ld ldb >= N): fp16 / bf16 with the
+ * 256 x 256 kernel only, both for a symmetric product, b_trans alone or
+ * both for a general one (anything else is NSG_ERR_INVALID_ARG);
  * operands, Cin and outputs are in `dtype`; batches are contiguous
  * ([batch][rows][ld]).  symmetric != 0 computes only the tiles on or below
  * the diagonal and mirrors them (requires M == N and out_t == NULL); the
@@ -230,7 +236,8 @@ nsg_status_t nsg_copy(const void *src, void *dst, size_t bytes, void *stream);
  * aligned. */
 nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch,
                          int64_t M, int64_t N, int64_t K,
-                         const void *A, int64_t lda, const void *B, int64_t ldb,
+                         const void *A, int64_t lda, int32_t a_trans,
+                         const void *B, int64_t ldb, int32_t b_trans,
                          float alpha, float beta, const void *Cin, int64_t ldc,
                          void *out, int64_t ldo, void *out_t, int64_t ldt,
                          void *out_d, float diag, int32_t tile, void *stream);

@@ -68,6 +68,8 @@ class LaunchInfo(ctypes.Structure):
         ("flops", ctypes.c_double),
         ("bytes", ctypes.c_double),
         ("label", ctypes.c_char * 24),
+        ("a_kmajor", ctypes.c_int32),
+        ("b_kmajor", ctypes.c_int32),
     ]
 
 
@@ -112,7 +114,7 @@ def lib() -> ctypes.CDLL:
     L.ns_timing_collect.restype = i32
     L.nsg_copy.argtypes = [vp, vp, sz, vp]
     L.nsg_copy.restype = i32
-    L.nsg_gemm_nt.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp, i64, f32, f32, vp, i64,
+    L.nsg_gemm_nt.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, i32, vp, i64, i32, f32, f32, vp, i64,
                               vp, i64, vp, i64, vp, f32, i32, vp]
     L.nsg_gemm_nt.restype = i32
     L.ns_select_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32, i32, P, ctypes.POINTER(sz)]
@@ -208,7 +210,8 @@ def plan(R: int, C: int, **kw):
     arr = (LaunchInfo * max(1, n.value))()
     _check(lib().ns_plan(R, C, ctypes.byref(p), arr, n.value, ctypes.byref(n)), "ns_plan")
     return [dict(kind=e.kind, kernel=KIND_NAMES[e.kind], step=e.step, M=e.M, N=e.N, K=e.K,
-                 flops=e.flops, bytes=e.bytes, label=e.label.decode()) for e in arr[:n.value]]
+                 flops=e.flops, bytes=e.bytes, label=e.label.decode(), a_kmajor=bool(e.a_kmajor),
+                 b_kmajor=bool(e.b_kmajor)) for e in arr[:n.value]]
 
 
 def nbytes(t: torch.Tensor) -> int:
@@ -351,14 +354,16 @@ def copy(src: torch.Tensor, dst: torch.Tensor):
 
 def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 0.0,
             Cin: Optional[torch.Tensor] = None, symmetric: bool = False, transposed_out: bool = False,
-            diag: Optional[float] = None, tile: int = 0):
+            diag: Optional[float] = None, tile: int = 0, a_kmajor: bool = False, b_kmajor: bool = False):
     """Library GEMM building block: V = alpha A B^T + beta Cin over a batch.
 
     A [b, M, K], B [b, N, K] (M, N, K multiples of 256) in one dtype; tile 128
-    or 256 picks the kernel (0: the library's choice).
+    or 256 picks the kernel (0: the library's choice).  With a_kmajor
+    (b_kmajor) A (B) is passed K-major instead, as [b, K, M] ([b, K, N]).
     Returns (V, V^T or None, V + diag I or None)."""
-    b, M, K = A.shape
-    N = B.shape[1]
+    b = A.shape[0]
+    M, K = (A.shape[2], A.shape[1]) if a_kmajor else (A.shape[1], A.shape[2])
+    N = B.shape[2] if b_kmajor else B.shape[1]
     for t in (A, B) + ((Cin,) if Cin is not None else ()):
         if t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
             raise ValueError("gemm_nt operands need unit column stride and packed batches")
@@ -368,7 +373,8 @@ def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
     with torch.cuda.device(A.device):
         code = lib().nsg_gemm_nt(_dtype_code(A.dtype), 1 if symmetric else 0, b, M, N, K,
-                                 ptr(A), A.stride(1), ptr(B), B.stride(1), float(alpha), float(beta), ptr(Cin),
+                                 ptr(A), A.stride(1), 1 if a_kmajor else 0, ptr(B), B.stride(1),
+                                 1 if b_kmajor else 0, float(alpha), float(beta), ptr(Cin),
                                  Cin.stride(1) if Cin is not None else N,
                                  ptr(out), N, ptr(out_t), M, ptr(out_d), float(diag or 0.0), int(tile),
                                  ctypes.c_void_p(_stream_handle(A.device)))

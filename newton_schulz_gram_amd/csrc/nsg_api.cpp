@@ -47,6 +47,7 @@ struct Launch {
   std::string label;
   int A = kNone, B = kNone, Cin = kNone, out0 = kNone, out1 = kNone, out2 = kNone;
   int M = 0, N = 0, K = 0, Mv = 0, Nv = 0;
+  int at = 0, bt = 0;  // operand stored K-major (K x M / K x N)
   float alpha = 1.f, beta = 0.f, diag = 0.f;
   int gpow = 0;
   bool final_out = false;
@@ -57,6 +58,9 @@ struct Plan {
   int64_t R = 0, C = 0, n = 0, m = 0, np = 0, mp = 0;
   bool tr = false;
   bool gram = false;
+  // one layout of X only (the input's own: X^T for tall inputs, X for wide
+  // ones); the products that need the other read it K-major
+  bool single = false;
   int T = 0;
   uint64_t restarts = 0;  // bit t-1: restart at the top of step t
   bool restart_at(int t) const { return t >= 1 && t <= 64 && ((restarts >> (t - 1)) & 1u); }
@@ -178,6 +182,7 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     else if (p->restart_after >= 1 && p->restart_after < P.T) P.restarts = 1ull << p->restart_after;
   }
   P.cfg = choose_cfg(P.np, P.mp, P.cdtype);
+  P.single = (P.cfg == kTile256) && (P.cdtype != NSG_F32);
   // power-of-two range shift f ~ log2(sqrt(n)): keeps X0 = X/||X||_F and
   // R0 = X0 X0^T away from fp16 subnormals (X0 entries ~ 1/sqrt(nm)).
   P.fexp = (int)std::floor(std::log2((double)P.n) / 2.0);
@@ -209,9 +214,12 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     Launch L; L.kind = 0; L.label = "norm_reduce"; L.bytes = (double)R * C * dtype_size(0); P.launches.push_back(L);
     Launch S; S.kind = 1; S.label = "scale_cast_T"; S.bytes = 0; P.launches.push_back(S);
   }
-  P.used[kX0] = P.used[kX0T] = true;
+  if (P.single) P.used[P.tr ? kX0T : kX0] = true;
+  else P.used[kX0] = P.used[kX0T] = true;
   const int last = P.T + 1;
   const int OUT = kOutUser;
+  const bool sgl = P.single, tr = P.tr;
+  auto kmajor = [&](int a, int b) { P.launches.back().at = a; P.launches.back().bt = b; };
 
   if (!P.gram) {
     // Algorithm 1: A = X X^T ; B = b A + c A^2 ; X = a X + B X.
@@ -221,20 +229,39 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     for (int t = 1; t <= P.T; ++t) {
       const double a = P.a[t - 1], b = P.b[t - 1], c = P.c[t - 1];
       // A_true = xs^2 r^(2 xpow) X_s X_s^T; stored A~ = A_true / xs^2
-      add_gemm(P, true, t, "A=XXt", X, X, kNone, kS0, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
-               2 * xpow, false);
+      if (sgl && tr) {  // A = X X^T from X^T read K-major
+        add_gemm(P, true, t, "A=XXt", XT, XT, kNone, kS0, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
+                 2 * xpow, false);
+        kmajor(1, 1);
+      } else {
+        add_gemm(P, true, t, "A=XXt", X, X, kNone, kS0, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
+                 2 * xpow, false);
+      }
       const double as = xs * xs;
       add_gemm(P, true, t, "B=bA+cA2", kS0, kS0, kS0, kS1, kNone, kNone, np, np, np, n, n, c * as * as,
                b * as, 0.0, 0, false);
       if (t < P.T) {
-        add_gemm(P, false, t, "X=aX+BX", kS1, XT, X, Xn, XnT, kNone, np, mp, np, n, m, xs, a * xs, 0.0,
-                 xpow, false);
+        if (sgl && tr) {  // X'^T = a X^T + X^T B (B exactly symmetric)
+          add_gemm(P, false, t, "Xt=aXt+XtB", XT, kS1, XT, XnT, kNone, kNone, mp, np, np, m, n, xs, a * xs, 0.0,
+                   xpow, false);
+        } else if (sgl) {  // X' = a X + B X with X read K-major
+          add_gemm(P, false, t, "X=aX+BX", kS1, X, X, Xn, kNone, kNone, np, mp, np, n, m, xs, a * xs, 0.0,
+                   xpow, false);
+          kmajor(0, 1);
+        } else {
+          add_gemm(P, false, t, "X=aX+BX", kS1, XT, X, Xn, XnT, kNone, np, mp, np, n, m, xs, a * xs, 0.0,
+                   xpow, false);
+        }
         std::swap(X, Xn);
         std::swap(XT, XnT);
       } else if (P.tr) {
         // X'^T = a X^T + X^T B (B exactly symmetric): NT with A = X^T, B = B
         add_gemm(P, false, last, "Yt=aXt+XtB", XT, kS1, XT, OUT, kNone, kNone, mp, np, np, m, n, xs,
                  a * xs, 0.0, xpow, true);
+      } else if (sgl) {
+        add_gemm(P, false, last, "Y=aX+BX", kS1, X, X, OUT, kNone, kNone, np, mp, np, n, m, xs, a * xs,
+                 0.0, xpow, true);
+        kmajor(0, 1);
       } else {
         add_gemm(P, false, last, "Y=aX+BX", kS1, XT, X, OUT, kNone, kNone, np, mp, np, n, m, xs, a * xs,
                  0.0, xpow, true);
@@ -250,19 +277,40 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     int Rb = kS0, Zb = kS1, Qcur = kNone, Qfree[2] = {kS2, kS3}, RZb = kS4, RZTb = kS5;
     const bool symu = p->sym_updates != 0;
     bool r_scaled = true;  // R_true = 2^-2f R_stored (only R0)
-    add_gemm(P, true, 0, "R0=XXt", kX0, kX0, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
-             false);
+    if (sgl && tr) {
+      add_gemm(P, true, 0, "R0=XXt", kX0T, kX0T, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
+               false);
+      kmajor(1, 1);
+    } else {
+      add_gemm(P, true, 0, "R0=XXt", kX0, kX0, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
+               false);
+    }
     for (int t = 1; t <= P.T; ++t) {
       const double a = P.a[t - 1], b = P.b[t - 1], c = P.c[t - 1];
       if (P.restart_at(t)) {
         // X <- Q X ; R <- X X^T ; Q <- I   (Alg. 3, "restart to stabilize");
         // repeated restarts alternate between the two X buffers
         const int Xn = (Xb == kX1) ? kX0 : kX1, XnT = (Xb == kX1) ? kX0T : kX1T;
-        add_gemm(P, false, t, "X=QX", Qcur, XbT, kNone, Xn, XnT, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
-                 xpow, false);
-        Xb = Xn; XbT = XnT; xs = 1.0; xpow = 0;
-        add_gemm(P, true, t, "R=XXt", Xb, Xb, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
-                 0, false);
+        if (sgl && tr) {  // X^T <- X^T Q^T, and R = X X^T from X^T read K-major
+          add_gemm(P, false, t, "Xt=XtQt", XbT, Qcur, kNone, XnT, kNone, kNone, mp, np, np, m, n, xs, 0.0, 0.0,
+                   xpow, false);
+          Xb = Xn; XbT = XnT; xs = 1.0; xpow = 0;
+          add_gemm(P, true, t, "R=XXt", XbT, XbT, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
+                   0, false);
+          kmajor(1, 1);
+        } else {
+          if (sgl) {  // X <- Q X with X read K-major
+            add_gemm(P, false, t, "X=QX", Qcur, Xb, kNone, Xn, kNone, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
+                     xpow, false);
+            kmajor(0, 1);
+          } else {
+            add_gemm(P, false, t, "X=QX", Qcur, XbT, kNone, Xn, XnT, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
+                     xpow, false);
+          }
+          Xb = Xn; XbT = XnT; xs = 1.0; xpow = 0;
+          add_gemm(P, true, t, "R=XXt", Xb, Xb, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0,
+                   0, false);
+        }
         r_scaled = false;
         Qcur = kNone;
       }
@@ -298,6 +346,10 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
       // Y^T = X^T Q^T : NT with A = X^T (m x n), B = Q
       add_gemm(P, false, last, "Yt=XtQt", XbT, Qcur, kNone, OUT, kNone, kNone, mp, np, np, m, n, xs, 0.0,
                0.0, xpow, true);
+    } else if (sgl) {
+      add_gemm(P, false, last, "Y=QX", Qcur, Xb, kNone, OUT, kNone, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
+               xpow, true);
+      kmajor(0, 1);
     } else {
       add_gemm(P, false, last, "Y=QX", Qcur, XbT, kNone, OUT, kNone, kNone, np, mp, np, n, m, xs, 0.0, 0.0,
                xpow, true);
@@ -494,6 +546,8 @@ nsg_status_t ns_plan(int64_t R, int64_t C, const nsg_params_t *p, nsg_launch_inf
     e.bytes = L.bytes;
     std::memset(e.label, 0, sizeof(e.label));
     std::strncpy(e.label, L.label.c_str(), sizeof(e.label) - 1);
+    e.a_kmajor = L.at;
+    e.b_kmajor = L.bt;
   }
   return NSG_OK;
 }
@@ -553,11 +607,13 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
       a.rows_p = (int32_t)(P.tr ? P.mp : P.np);
       a.cols_p = (int32_t)(P.tr ? P.np : P.mp);
       a.same = P.tr ? ptr(kX0T) : ptr(kX0);
-      a.swap = P.tr ? ptr(kX0) : ptr(kX0T);
+      a.swap = P.single ? nullptr : (P.tr ? ptr(kX0) : ptr(kX0T));
       a.ld_same = P.tr ? P.ld[kX0T] : P.ld[kX0];
-      a.ld_swap = P.tr ? P.ld[kX0] : P.ld[kX0T];
       a.s_same = elem_stride(P, P.tr ? kX0T : kX0);
-      a.s_swap = elem_stride(P, P.tr ? kX0 : kX0T);
+      if (!P.single) {
+        a.ld_swap = P.tr ? P.ld[kX0] : P.ld[kX0T];
+        a.s_swap = elem_stride(P, P.tr ? kX0 : kX0T);
+      }
       a.cdtype = P.cdtype;
       a.gscale = reinterpret_cast<float *>(ptr(kGScale));
       a.status = status;
@@ -567,6 +623,7 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
       GemmArgs a;
       a.A = ptr(L.A); a.lda = P.ld[L.A]; a.sA = elem_stride(P, L.A);
       a.B = ptr(L.B); a.ldb = P.ld[L.B]; a.sB = elem_stride(P, L.B);
+      a.a_trans = L.at; a.b_trans = L.bt;
       if (L.Cin >= 0) { a.Cin = ptr(L.Cin); a.ldc = P.ld[L.Cin]; a.sC = elem_stride(P, L.Cin); }
       if (L.out0 == kOutUser) {
         a.out0 = out;
@@ -659,9 +716,9 @@ nsg_status_t nsg_copy(const void *src, void *dst, size_t bytes, void *stream) {
 }
 
 nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_t M, int64_t N, int64_t K,
-                         const void *A, int64_t lda, const void *B, int64_t ldb, float alpha, float beta,
-                         const void *Cin, int64_t ldc, void *out, int64_t ldo, void *out_t, int64_t ldt,
-                         void *out_d, float diag, int32_t tile, void *stream) {
+                         const void *A, int64_t lda, int32_t a_trans, const void *B, int64_t ldb, int32_t b_trans,
+                         float alpha, float beta, const void *Cin, int64_t ldc, void *out, int64_t ldo, void *out_t,
+                         int64_t ldt, void *out_d, float diag, int32_t tile, void *stream) {
   if (!valid_dtype(dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
   if (tile != 0 && tile != 128 && tile != 256) return NSG_ERR_INVALID_ARG;
   if (batch < 0 || M < 0 || N < 0 || K < 0) return NSG_ERR_SHAPE;
@@ -670,7 +727,13 @@ nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_
       K > NSG_MAX_SIDE)
     return NSG_ERR_SHAPE;
   if (A == nullptr || B == nullptr) return NSG_ERR_INVALID_ARG;
-  if (lda < K || ldb < K) return NSG_ERR_SHAPE;
+  if ((a_trans != 0 && a_trans != 1) || (b_trans != 0 && b_trans != 1)) return NSG_ERR_INVALID_ARG;
+  // K-major operands: 16-bit 256 x 256 kernel; both (symmetric or general)
+  // or B alone (general)
+  if ((a_trans || b_trans) &&
+      (dtype == NSG_F32 || tile == 128 || (a_trans && !b_trans) || (symmetric && a_trans != b_trans)))
+    return NSG_ERR_INVALID_ARG;
+  if (lda < (a_trans ? M : K) || ldb < (b_trans ? N : K)) return NSG_ERR_SHAPE;
   if (symmetric && (M != N || out_t != nullptr)) return NSG_ERR_INVALID_ARG;
   if (!symmetric && out_d != nullptr) return NSG_ERR_INVALID_ARG;
   if (Cin != nullptr && ldc < N) return NSG_ERR_SHAPE;
@@ -679,8 +742,9 @@ nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_
   const size_t es = dtype_size(dtype);
   if ((lda * (int64_t)es) % 16 || (ldb * (int64_t)es) % 16) return NSG_ERR_SHAPE;
   GemmArgs a;
-  a.A = A; a.lda = lda; a.sA = M * lda;
-  a.B = B; a.ldb = ldb; a.sB = N * ldb;
+  a.A = A; a.lda = lda; a.sA = (a_trans ? K : M) * lda;
+  a.B = B; a.ldb = ldb; a.sB = (b_trans ? K : N) * ldb;
+  a.a_trans = a_trans; a.b_trans = b_trans;
   if (Cin) { a.Cin = Cin; a.ldc = ldc; a.sC = M * ldc; }
   a.out0 = out; a.ld0 = ldo; a.s0 = M * ldo; a.out0_dtype = dtype; a.out0_pad = 1;
   if (out_t) { a.out1 = out_t; a.ld1 = ldt; a.s1 = N * ldt; }
@@ -689,6 +753,7 @@ nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_
   a.alpha = alpha; a.beta = beta;
   a.batch = (int32_t)batch;
   const int cfg = tile == 0 ? choose_cfg(M, N, dtype) : (tile == 256 ? kTile256 : kTile128);
+  if ((a_trans || b_trans) && cfg != kTile256) return NSG_ERR_INVALID_ARG;
   return launch_gemm(dtype, symmetric != 0, cfg, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? NSG_OK
              : NSG_ERR_HIP;

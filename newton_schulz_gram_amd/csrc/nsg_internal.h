@@ -25,12 +25,16 @@ enum BufferKind : int { kOutUser = -2, kNone = -1 };
 // alpha' = alpha * gscale[b]^gpow and beta' = beta * gscale[b]^gpow.
 // A is M x K (lda), B is N x K (ldb), Cin is M x N (ldc), all in the compute
 // dtype, batches `s*` elements apart.  M, N, K are padded sizes (multiples of
-// the tile); Mv x Nv is the valid corner.
+// the tile); Mv x Nv is the valid corner.  a_trans / b_trans: the operand is
+// stored K-major instead, as K x M (lda >= M) or K x N (ldb >= N) (16-bit
+// 256 x 256 kernel only: both for symmetric products, b_trans alone for
+// general ones).
 struct GemmArgs {
   const void *A = nullptr;
   int64_t lda = 0, sA = 0;
   const void *B = nullptr;
   int64_t ldb = 0, sB = 0;
+  int32_t a_trans = 0, b_trans = 0;
   const void *Cin = nullptr;
   int64_t ldc = 0, sC = 0;
   // out0: V (row-major, mirrored for symmetric launches).  Its dtype may be

@@ -109,7 +109,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p, const f32x16 (&acc)[
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         float x = alpha * acc[i][j][r];
-        if (cin != nullptr) x += beta * (float)cin[(size_t)row * p.ldc + col];
+        if (cin != nullptr) x = __builtin_fmaf(beta, (float)cin[(size_t)row * p.ldc + col], x);
         v[r] = (row < p.Mv && col < p.Nv) ? x : 0.f;
       }
 #pragma unroll
@@ -507,8 +507,10 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
       for (int r = 0; r < 8; ++r)
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
+          // one fixed rounding: fma(beta', Cin, alpha' acc), whatever the
+          // compiler would contract
           float x = alpha * v[r][c];
-          if constexpr (CIN) x += beta * (float)cinv[it][r][c / VT][c % VT];
+          if constexpr (CIN) x = __builtin_fmaf(beta, (float)cinv[it][r][c / VT][c % VT], x);
           v[r][c] = x;
         }
       if (!full) {
@@ -880,7 +882,29 @@ template <> struct Mfma16<NSG_BF16> {
   }
 };
 
-template <int DT, bool SYM, bool CIN>
+// Operands in their K-major layout (AT / BT): the operand is stored as
+// K x 256-wide rows (the M or N index contiguous, pitch lda / ldb), and a
+// stage is 64 K-rows of 512 bytes.  Direct-load instruction i of wave w
+// fills K-rows 2 (w + 4 i) and 2 (w + 4 i) + 1; inside a row the 16 blocks
+// of 16 columns (32 bytes) are permuted, physical block = logical block ^
+// g(row), g(row) = (row & 3) | ((row >> 3) & 1) << 2.  A fragment (16
+// columns, 8 consecutive K) is two ds_read_b64_tr_b16: lane j of each group
+// of 16 points at K-row kb + j / 4, columns 4 (j % 4) .. + 3 of the block,
+// and lane n receives the 4 consecutive K values kb .. kb + 3 of column n.
+// The 8 K-rows a group of 32 lanes reads then fall on 8 distinct 32-byte
+// block slots: one pass over the 64 banks, no conflict.
+__device__ __forceinline__ int trg(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_t;
+template <typename F>
+__device__ __forceinline__ F tr_frag(const unsigned char *p0, const unsigned char *p1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(F, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int DT, bool SYM, bool CIN, bool AT, bool BT>
 __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   using MF = Mfma16<DT>;
   using T = typename MF::T;
@@ -910,31 +934,50 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   // direct-load sources: wave w fills the 1 KB blocks b = w + 4 i of each
   // slice (rows 8 b .. 8 b + 7; lane l writes chunk slot l % 8 of row
   // 8 b + l / 8, which holds logical chunk (l % 8) ^ ((row >> 1) & 7))
-  const T *gA = reinterpret_cast<const T *>(p.A) + (size_t)g * p.sA + (size_t)tm * 256 * p.lda;
-  const T *gB = reinterpret_cast<const T *>(p.B) + (size_t)g * p.sB + (size_t)tn * 256 * p.ldb;
+  const T *gA = reinterpret_cast<const T *>(p.A) + (size_t)g * p.sA + (AT ? (size_t)tm * 256 : (size_t)tm * 256 * p.lda);
+  const T *gB = reinterpret_cast<const T *>(p.B) + (size_t)g * p.sB + (BT ? (size_t)tn * 256 : (size_t)tn * 256 * p.ldb);
+  // Per-lane offsets are rederived for every tile from a copy of the lane
+  // index the compiler cannot see through, so they are never kept (and
+  // spilled) across the epilogue.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  auto dma_off = [&](bool trans, int i, int64_t ld) -> unsigned {
+    if (trans) {  // K-row 2 (w + 4 i) + ln / 32, physical 16-byte chunk ln % 32
+      const int row = 2 * (wave + NW * i) + (ln >> 5), pc = ln & 31;
+      return (unsigned)((row * (int)ld + (((pc >> 1) ^ trg(row)) << 4) + ((pc & 1) << 3)) * 2);
+    }
+    const int row = (wave + NW * i) * 8 + (ln >> 3);
+    return (unsigned)((row * (int)ld + (((ln & 7) ^ ((row >> 1) & 7)) << 3)) * 2);
+  };
   unsigned offA[NLD], offB[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int row = (wave + NW * i) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    offA[i] = (unsigned)((row * (int)p.lda + chunk * 8) * 2);
-    offB[i] = (unsigned)((row * (int)p.ldb + chunk * 8) * 2);
+    offA[i] = dma_off(AT, i, p.lda);
+    offB[i] = dma_off(BT, i, p.ldb);
   }
   const int nk = p.K / BK;  // >= 4: K is a multiple of 256
+  // stage kt of each operand: 64 K elements of every row, or 64 K-rows
+  const size_t stepA = AT ? (size_t)BK * p.lda : (size_t)BK, stepB = BT ? (size_t)BK * p.ldb : (size_t)BK;
   auto dma = [&](int kt, int slot, int q) {  // q-th of the 16 loads of a stage: pair q / 2, operand q % 2
     unsigned char *st = lds + slot * STAGE;
     const int i = q >> 1;
-    if (q & 1) lds_dma16(gB + (size_t)kt * BK, offB[i], st + SLICE + (wave + NW * i) * 1024);
-    else lds_dma16(gA + (size_t)kt * BK, offA[i], st + (wave + NW * i) * 1024);
+    if (q & 1) lds_dma16(gB + (size_t)kt * stepB, offB[i], st + SLICE + (wave + NW * i) * 1024);
+    else lds_dma16(gA + (size_t)kt * stepA, offA[i], st + (wave + NW * i) * 1024);
   };
 
   // fragment reads: lane l reads row (block row + l % 16), K elements
   // 32 s + 8 (l / 16) .. + 7 of the stage; block i adds i * 2048 bytes
-  const int r16 = lane & 15, q4 = lane >> 4;
+  const int r16 = ln & 15, q4 = ln >> 4;
   const int rA = wm * 128 + r16, rB = wn * 128 + r16;
   const int zA = (rA >> 1) & 7, zB = (rB >> 1) & 7;
   const int fA0 = rA * 128 + ((q4 ^ zA) << 4), fA1 = rA * 128 + (((4 + q4) ^ zA) << 4);
   const int fB0 = SLICE + rB * 128 + ((q4 ^ zB) << 4), fB1 = SLICE + rB * 128 + (((4 + q4) ^ zB) << 4);
+  // K-major operands: lane (q4, r16) reads K-row kr = 8 q4 + r16 / 4 (+ 4 for
+  // the second read, + 32 for the second K half), columns 4 (r16 % 4) of
+  // block i: byte (kr * 512 + 256 wq + 8 (r16 % 4)) ^ ((i ^ g(kr)) << 5)
+  const int kr = 8 * q4 + (r16 >> 2);
+  const int tA = kr * 512 + wm * 256 + (r16 & 3) * 8 + (trg(kr) << 5);
+  const int tB = SLICE + kr * 512 + wn * 256 + (r16 & 3) * 8 + (trg(kr) << 5);
 
   f32x4 acc[8][8];
 #pragma unroll
@@ -943,12 +986,24 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   frag_t a[8][2], b[8][2];
   auto rd_a = [&](const unsigned char *st, int i) {
-    a[i][0] = *reinterpret_cast<const frag_t *>(st + fA0 + i * 2048);
-    a[i][1] = *reinterpret_cast<const frag_t *>(st + fA1 + i * 2048);
+    if constexpr (AT) {
+      const unsigned char *q = st + (tA ^ (i << 5));
+      a[i][0] = tr_frag<frag_t>(q, q + 2048);
+      a[i][1] = tr_frag<frag_t>(q + 16384, q + 18432);
+    } else {
+      a[i][0] = *reinterpret_cast<const frag_t *>(st + fA0 + i * 2048);
+      a[i][1] = *reinterpret_cast<const frag_t *>(st + fA1 + i * 2048);
+    }
   };
   auto rd_b = [&](const unsigned char *st, int j) {
-    b[j][0] = *reinterpret_cast<const frag_t *>(st + fB0 + j * 2048);
-    b[j][1] = *reinterpret_cast<const frag_t *>(st + fB1 + j * 2048);
+    if constexpr (BT) {
+      const unsigned char *q = st + (tB ^ (j << 5));
+      b[j][0] = tr_frag<frag_t>(q, q + 2048);
+      b[j][1] = tr_frag<frag_t>(q + 16384, q + 18432);
+    } else {
+      b[j][0] = *reinterpret_cast<const frag_t *>(st + fB0 + j * 2048);
+      b[j][1] = *reinterpret_cast<const frag_t *>(st + fB1 + j * 2048);
+    }
   };
   auto pair = [&](int i, int j) {
     acc[i][j] = MF::mma(a[i][0], b[j][0], acc[i][j]);
@@ -1086,16 +1141,29 @@ static hipError_t launch_256(const GemmArgs &a, hipStream_t s) {
     const unsigned ncu = cu_count();
     if (ncu == 0) return hipErrorInvalidDevice;
     const unsigned grid = blocks < ncu ? (unsigned)blocks : ncu;
-    if (a.Cin != nullptr)
-      hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, true>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, false>), dim3(grid), dim3(256), 0, s, a);
+    // operand layouts: both row-major (NT), both K-major (the Gram product
+    // of a K-major X), or a K-major B (general products Q X of a row-major X)
+    if (a.a_trans != a.b_trans && (SYM || a.a_trans)) return hipErrorInvalidValue;
+    const int mode = a.a_trans ? 2 : (a.b_trans ? 1 : 0);
+#define NSG_H(C, AT_, BT_) hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, C, AT_, BT_>), dim3(grid), dim3(256), 0, s, a)
+    if (a.Cin != nullptr) {
+      if (mode == 0) NSG_H(true, false, false);
+      else if (mode == 1) NSG_H(true, false, true);
+      else NSG_H(true, true, true);
+    } else {
+      if (mode == 0) NSG_H(false, false, false);
+      else if (mode == 1) NSG_H(false, false, true);
+      else NSG_H(false, true, true);
+    }
+#undef NSG_H
   }
   return hipGetLastError();
 }
 
 template <int DT, bool SYM>
 static hipError_t launch_cfg(int cfg, const GemmArgs &a, hipStream_t s) {
+  // K-major operands exist only on the 16-bit 256 x 256 kernel
+  if ((a.a_trans || a.b_trans) && (cfg != kTile256 || DT == NSG_F32)) return hipErrorInvalidValue;
   if (cfg == kTile256) return launch_256<DT, SYM>(a, s);
   return launch_one<DT, 128, 128, 2, 2, SYM>(a, s);
 }
@@ -1272,7 +1340,7 @@ __global__ void __launch_bounds__(256) scale_cast_transpose_kernel(const ScaleAr
 // written as 128-byte rows: a thread takes two adjacent input columns (one
 // 4-byte LDS word per row) and 8 input rows.  Every output element is
 // cvt(ldexp(x, e)), as in the kernel above.
-template <typename TI, typename TO, bool VEC>
+template <typename TI, typename TO, bool VEC, bool SWAP>
 __global__ void __launch_bounds__(256) scale_cast_transpose16_kernel(const ScaleArgs p) {
   static_assert(sizeof(TO) == 2, "16-bit outputs");
   constexpr int PW = 65;  // LDS row pitch in 32-bit words (two outputs each)
@@ -1310,11 +1378,13 @@ __global__ void __launch_bounds__(256) scale_cast_transpose16_kernel(const Scale
 #pragma unroll
     for (int q = 0; q < 8; ++q) w[q] = cvt<TO>(ldexpf(v[q], e));
     *reinterpret_cast<vout_t *>(same + (size_t)row * p.ld_same + col) = w;
+    if constexpr (!SWAP) continue;
     const u16x8 bits = __builtin_bit_cast(u16x8, w);
     uint32_t *t = tile + a * PW + (cl >> 1);
 #pragma unroll
     for (int u = 0; u < 4; ++u) t[u] = (uint32_t)bits[2 * u] | ((uint32_t)bits[2 * u + 1] << 16);
   }
+  if constexpr (!SWAP) return;  // one layout only
   __syncthreads();
   const int ac = 8 * (tid & 7);
 #pragma unroll
@@ -1336,9 +1406,16 @@ template <typename TI, bool VEC>
 static void launch_scale_in(const ScaleArgs &a, dim3 grid, hipStream_t s) {
   // 16-bit outputs: 64 x 128 tiles (the padded column count is a multiple of 256)
   const dim3 grid16(grid.x / 2, grid.y, grid.z);
+  const bool swap = a.swap != nullptr;
   switch (a.cdtype) {
-    case NSG_F16: hipLaunchKernelGGL((scale_cast_transpose16_kernel<TI, _Float16, VEC>), grid16, dim3(256), 0, s, a); break;
-    case NSG_BF16: hipLaunchKernelGGL((scale_cast_transpose16_kernel<TI, __bf16, VEC>), grid16, dim3(256), 0, s, a); break;
+    case NSG_F16:
+      if (swap) hipLaunchKernelGGL((scale_cast_transpose16_kernel<TI, _Float16, VEC, true>), grid16, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((scale_cast_transpose16_kernel<TI, _Float16, VEC, false>), grid16, dim3(256), 0, s, a);
+      break;
+    case NSG_BF16:
+      if (swap) hipLaunchKernelGGL((scale_cast_transpose16_kernel<TI, __bf16, VEC, true>), grid16, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((scale_cast_transpose16_kernel<TI, __bf16, VEC, false>), grid16, dim3(256), 0, s, a);
+      break;
     default: hipLaunchKernelGGL((scale_cast_transpose_kernel<TI, float, VEC>), grid, dim3(256), 0, s, a); break;
   }
 }

@@ -91,8 +91,9 @@ int main(int argc, char **argv) {
       const int64_t n = (G < (1 << 20) && R < (1 << 20)) ? G * R : std::numeric_limits<int64_t>::max();
       EXPECT(ns_muon_momentum(nullptr, idt, dummy, odt, n, 0.9f, nullptr) != NSG_OK);
       EXPECT(ns_muon_update(nullptr, idt, dummy, odt, n, 0.01, 0.0, 1.0, 1, 1, 1, nullptr) != NSG_OK);
-      EXPECT(nsg_gemm_nt(idt, (int32_t)(rng() % 2), G, R, C, R, nullptr, R, nullptr, R, 1.f, 0.f, nullptr, R,
-                         nullptr, C, nullptr, R, nullptr, 0.f, 0, nullptr) != NSG_OK);
+      EXPECT(nsg_gemm_nt(idt, (int32_t)(rng() % 2), G, R, C, R, nullptr, R, (int32_t)(rng() % 3), nullptr, R,
+                         (int32_t)(rng() % 3), 1.f, 0.f, nullptr, R, nullptr, C, nullptr, R, nullptr, 0.f, 0,
+                         nullptr) != NSG_OK);
     }
     (void)ns_status_string((nsg_status_t)pick({-1, 0, 1, 2, 3, 4, 5, 6, 1000}));
   }

@@ -119,3 +119,51 @@ def test_tile_schedule_covers_every_tile(dtype, kind, batch, n):
     d = (out.float() - ref).view(batch, n // 256, 256, n // 256, 256).norm(dim=(2, 4))
     r = ref.view(batch, n // 256, 256, n // 256, 256).norm(dim=(2, 4))
     assert float((d / r).max()) <= 4 * TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("n,K,batch", [(512, 768, 3), (1024, 2048, 2), (4352, 512, 1)])
+def test_kmajor_symmetric_gram_matches_row_major(dtype, n, K, batch):
+    """X X^T with X passed K-major (as X^T, K x n): the transposed LDS reads
+    hand the MFMAs the same fragments as the row-major path, so the result is
+    bit for bit the same (and exactly symmetric)."""
+    g = torch.Generator(device="cuda").manual_seed(21)
+    X = torch.randn(batch, n, K, device="cuda", generator=g).to(dtype)
+    Xt = X.transpose(1, 2).contiguous()
+    ref, _, _ = nsg.gemm_nt(X, X, alpha=0.75, symmetric=True, tile=256)
+    out, _, _ = nsg.gemm_nt(Xt, Xt, alpha=0.75, symmetric=True, tile=256, a_kmajor=True, b_kmajor=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert rel(out, ref_nt(X, X, 0.75)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("MNK", [(512, 768, 256), (768, 2048, 512), (256, 4352, 1024)])
+@pytest.mark.parametrize("both", [False, True])
+def test_kmajor_general_matches_row_major(dtype, MNK, both):
+    """A B^T with B (and A) passed K-major, with Cin and the transposed copy:
+    bit for bit the row-major result."""
+    M, N, K = MNK
+    g = torch.Generator(device="cuda").manual_seed(22)
+    A = torch.randn(2, M, K, device="cuda", generator=g).to(dtype)
+    B = torch.randn(2, N, K, device="cuda", generator=g).to(dtype)
+    Cin = torch.randn(2, M, N, device="cuda", generator=g).to(dtype)
+    ref, ref_t, _ = nsg.gemm_nt(A, B, alpha=-0.5, beta=1.25, Cin=Cin, transposed_out=True, tile=256)
+    Ak = A.transpose(1, 2).contiguous() if both else A
+    out, out_t, _ = nsg.gemm_nt(Ak, B.transpose(1, 2).contiguous(), alpha=-0.5, beta=1.25, Cin=Cin,
+                                transposed_out=True, tile=256, a_kmajor=both, b_kmajor=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(out_t, ref_t)
+    assert rel(out, ref_nt(A, B, -0.5, 1.25, Cin)) <= TOL[dtype]
+
+
+def test_kmajor_rejected_where_unsupported():
+    A = torch.zeros(1, 512, 512, device="cuda", dtype=torch.float16)
+    with pytest.raises(nsg.NSGError):   # A alone K-major
+        nsg.gemm_nt(A, A, tile=256, a_kmajor=True)
+    with pytest.raises(nsg.NSGError):   # symmetric with one K-major operand
+        nsg.gemm_nt(A, A, symmetric=True, tile=256, b_kmajor=True)
+    with pytest.raises(nsg.NSGError):   # 128 x 128 kernel
+        nsg.gemm_nt(A, A, tile=128, b_kmajor=True)
+    with pytest.raises(nsg.NSGError):   # fp32
+        nsg.gemm_nt(A.float(), A.float(), tile=256, b_kmajor=True)

@@ -137,7 +137,8 @@ def test_gram_plan_structure():
         steps.setdefault(e["step"], []).append(e["label"])
     assert steps[1] == ["Z (+Q=Z+aI)", "RZ=RZ+aR", "R=Z.RZ+aRZ"]
     assert steps[2] == ["Z=bR+cR2", "Q=QZ+aQ"]
-    assert steps[3] == ["X=QX", "R=XXt", "Z (+Q=Z+aI)", "RZ=RZ+aR", "R=Z.RZ+aRZ"]
+    # tall input: only X^T is kept, so the restart forms X^T = X^T Q^T
+    assert steps[3] == ["Xt=XtQt", "R=XXt", "Z (+Q=Z+aI)", "RZ=RZ+aR", "R=Z.RZ+aRZ"]
     assert steps[5] == ["Z=bR+cR2", "Q=QZ+aQ"]
     assert steps[6] == ["Yt=XtQt"]  # tall input: output written as Y^T, i.e. R x C
     assert [e["label"] for e in nsg.plan(768, 3072)][-1] == "Y=QX"
@@ -322,3 +323,30 @@ def test_noalloc_rejects_before_any_gpu_call():
     # an empty bucket is a no-op
     assert L.ns_orthogonalize_noalloc(None, 0, None, 0, 0, 64, 128, ctypes.byref(p), None, None) == 0
     assert "NSG_NOALLOC_MAX_BYTES (128u << 20)" in open(HEADER).read()
+
+
+def test_single_layout_plan():
+    """The 16-bit 256 x 256 path keeps X in one layout only (the input's own):
+    a tall input's Gram products read X^T K-major, a wide input's Q X reads X
+    K-major, and no transposed copy of X is stored; the fp32 path and small n
+    (128 x 128 kernel) keep both layouts and row-major operands only."""
+    def km(P):
+        return {e["label"]: (e["a_kmajor"], e["b_kmajor"]) for e in P if e["kernel"].startswith("gemm")}
+    tall = km(nsg.plan(11008, 4096))
+    assert tall["R0=XXt"] == (True, True) and tall["R=XXt"] == (True, True)
+    assert tall["Xt=XtQt"] == (False, False) and tall["Yt=XtQt"] == (False, False)
+    assert all(v == (False, False) for k, v in tall.items() if k not in ("R0=XXt", "R=XXt"))
+    wide = km(nsg.plan(768, 3072))
+    assert wide["X=QX"] == (False, True) and wide["Y=QX"] == (False, True)
+    assert wide["R0=XXt"] == (False, False) and wide["R=XXt"] == (False, False)
+    sq = nsg.plan(4096, 4096)
+    assert all(e["b_kmajor"] and not e["a_kmajor"] for e in sq if e["label"] in ("X=aX+BX", "Y=aX+BX"))
+    tall_std = km(nsg.plan(4096, 1024, mode="standard"))
+    assert tall_std["A=XXt"] == (True, True) and tall_std["Xt=aXt+XtB"] == (False, False)
+    for P in (nsg.plan(11008, 4096, compute_dtype="f32"), nsg.plan(200, 1000)):
+        assert not any(e["a_kmajor"] or e["b_kmajor"] for e in P)
+    # one copy of X (and of X after the restart) instead of two
+    n, m, es = 4096, 11008, 2
+    x_bytes = m * (n + 64) * es
+    assert nsg.workspace_size(1, 11008, 4096) < 2 * x_bytes + 6 * n * (n + 64) * es
+    assert nsg.workspace_size(1, 11008, 4096, compute_dtype="f32") > 4 * m * n * 4
