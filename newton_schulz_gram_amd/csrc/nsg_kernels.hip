@@ -579,19 +579,48 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
               if (o2 != nullptr) st_stream(w, reinterpret_cast<vt_t *>(b2c + (size_t)c * p.ld2 + e * VT));
             }
         }
-      } else if (cls == 1) {  // on the diagonal: the lower half, to both places
+      } else if (cls == 1) {
+        // On the diagonal: the block is made exactly symmetric from its lower
+        // half (w[r][c] = v[max(r, c)][min(r, c)]) and stored as 8 rows; its
+        // transposed place is itself.  Every element gets the value the lower
+        // half holds, as if the lower half were stored to both places, with
+        // whole-row stores instead of one store per element.
+        float w[8][8];
 #pragma unroll
         for (int r = 0; r < 8; ++r)
 #pragma unroll
-          for (int c = 0; c <= r; ++c) {
-            if (o0 != nullptr) st_stream(cvt<TO>(v[r][c]), b0 + (size_t)r * p.ld0 + c);
-            if (r > c) st_stream(cvt<T>(v[r][c]), bt + (size_t)c * ldt + r);
-            if (o2 != nullptr) {
-              const T d = cvt<T>((r == c && grow + r < p.Mv) ? v[r][c] + p.diag : v[r][c]);
-              st_stream(d, b2r + (size_t)r * p.ld2 + c);
-              if (r > c) st_stream(d, b2c + (size_t)c * p.ld2 + r);
-            }
+          for (int c = 0; c < 8; ++c) w[r][c] = c <= r ? v[r][c] : v[c][r];
+        if (o0 != nullptr) {
+          if (vec0 && full) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+              for (int e = 0; e < 8 / VO; ++e) {
+                vo_t x;
+#pragma unroll
+                for (int q = 0; q < VO; ++q) x[q] = cvt<TO>(w[r][e * VO + q]);
+                st_stream(x, reinterpret_cast<vo_t *>(b0 + (size_t)r * p.ld0 + e * VO));
+              }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+              for (int c = 0; c < 8; ++c)
+                if (pad0 || (grow + r < p.Mv && gcol + c < p.Nv))
+                  st_stream(cvt<TO>(w[r][c]), b0 + (size_t)r * p.ld0 + c);
           }
+        }
+        if (o2 != nullptr) {  // + diag on the valid diagonal
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            vt_t x[NV];
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+              x[c / VT][c % VT] = cvt<T>((r == c && grow + r < p.Mv) ? w[r][c] + p.diag : w[r][c]);
+#pragma unroll
+            for (int e = 0; e < NV; ++e) st_stream(x[e], reinterpret_cast<vt_t *>(b2r + (size_t)r * p.ld2 + e * VT));
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
