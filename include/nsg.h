@@ -232,15 +232,18 @@ nsg_status_t nsg_copy(const void *src, void *dst, size_t bytes, void *stream);
  * result is then exactly symmetric (the symmetric GEMM of the Dion3 paper,
  * Section 5 and Appendix C.1).  M, N and K must be multiples of 256.
  * tile selects the kernel: 128 or 256 (output tile edge), 0 = as
- * ns_orthogonalize would choose.  All pointers are device memory, 16-byte
- * aligned. */
+ * ns_orthogonalize would choose.  status (device, batch int32, or NULL):
+ * set to 1 for a batch whose out contains a non-finite value after rounding
+ * to `dtype` (entries of the others are left as they are).  All pointers are
+ * device memory, 16-byte aligned. */
 nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch,
                          int64_t M, int64_t N, int64_t K,
                          const void *A, int64_t lda, int32_t a_trans,
                          const void *B, int64_t ldb, int32_t b_trans,
                          float alpha, float beta, const void *Cin, int64_t ldc,
                          void *out, int64_t ldo, void *out_t, int64_t ldt,
-                         void *out_d, float diag, int32_t tile, void *stream);
+                         void *out_d, float diag, int32_t tile, int32_t *status,
+                         void *stream);
 
 /* ---- Dion3 selection front-end --------------------------------------------
  * Dion3 paper, Section 6 ("Selection", "Orthogonalization") and Algorithm 4,

@@ -115,7 +115,7 @@ def lib() -> ctypes.CDLL:
     L.nsg_copy.argtypes = [vp, vp, sz, vp]
     L.nsg_copy.restype = i32
     L.nsg_gemm_nt.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, i32, vp, i64, i32, f32, f32, vp, i64,
-                              vp, i64, vp, i64, vp, f32, i32, vp]
+                              vp, i64, vp, i64, vp, f32, i32, vp, vp]
     L.nsg_gemm_nt.restype = i32
     L.ns_select_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32, i32, P, ctypes.POINTER(sz)]
     L.ns_select_workspace_size.restype = i32
@@ -354,7 +354,8 @@ def copy(src: torch.Tensor, dst: torch.Tensor):
 
 def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 0.0,
             Cin: Optional[torch.Tensor] = None, symmetric: bool = False, transposed_out: bool = False,
-            diag: Optional[float] = None, tile: int = 0, a_kmajor: bool = False, b_kmajor: bool = False):
+            diag: Optional[float] = None, tile: int = 0, a_kmajor: bool = False, b_kmajor: bool = False,
+            status: Optional[torch.Tensor] = None):
     """Library GEMM building block: V = alpha A B^T + beta Cin over a batch.
 
     A [b, M, K], B [b, N, K] (M, N, K multiples of 256) in one dtype; tile 128
@@ -376,7 +377,7 @@ def gemm_nt(A: torch.Tensor, B: torch.Tensor, alpha: float = 1.0, beta: float = 
                                  ptr(A), A.stride(1), 1 if a_kmajor else 0, ptr(B), B.stride(1),
                                  1 if b_kmajor else 0, float(alpha), float(beta), ptr(Cin),
                                  Cin.stride(1) if Cin is not None else N,
-                                 ptr(out), N, ptr(out_t), M, ptr(out_d), float(diag or 0.0), int(tile),
+                                 ptr(out), N, ptr(out_t), M, ptr(out_d), float(diag or 0.0), int(tile), ptr(status),
                                  ctypes.c_void_p(_stream_handle(A.device)))
     _check(code, "nsg_gemm_nt")
     return out, out_t, out_d

@@ -718,7 +718,7 @@ nsg_status_t nsg_copy(const void *src, void *dst, size_t bytes, void *stream) {
 nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_t M, int64_t N, int64_t K,
                          const void *A, int64_t lda, int32_t a_trans, const void *B, int64_t ldb, int32_t b_trans,
                          float alpha, float beta, const void *Cin, int64_t ldc, void *out, int64_t ldo, void *out_t,
-                         int64_t ldt, void *out_d, float diag, int32_t tile, void *stream) {
+                         int64_t ldt, void *out_d, float diag, int32_t tile, int32_t *status, void *stream) {
   if (!valid_dtype(dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
   if (tile != 0 && tile != 128 && tile != 256) return NSG_ERR_INVALID_ARG;
   if (batch < 0 || M < 0 || N < 0 || K < 0) return NSG_ERR_SHAPE;
@@ -752,6 +752,7 @@ nsg_status_t nsg_gemm_nt(int32_t dtype, int32_t symmetric, int64_t batch, int64_
   a.M = (int32_t)M; a.N = (int32_t)N; a.K = (int32_t)K; a.Mv = (int32_t)M; a.Nv = (int32_t)N;
   a.alpha = alpha; a.beta = beta;
   a.batch = (int32_t)batch;
+  a.status = status;
   const int cfg = tile == 0 ? choose_cfg(M, N, dtype) : (tile == 256 ? kTile256 : kTile128);
   if ((a_trans || b_trans) && cfg != kTile256) return NSG_ERR_INVALID_ARG;
   return launch_gemm(dtype, symmetric != 0, cfg, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess

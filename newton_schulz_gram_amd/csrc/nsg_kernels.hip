@@ -437,6 +437,14 @@ __device__ __forceinline__ void stage_acc(const f32x4 (&acc)[8][TN], float *lds,
           make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
 }
 
+// Bits of the smallest positive fp32 value that rounds (to nearest even) to
+// infinity in TO: 65520 for fp16, 0x1.FFp127 for bf16 (halfway above the
+// largest bf16, and a tie rounds to the even infinity), +inf for fp32.
+template <typename TO> __device__ __forceinline__ constexpr unsigned overflow_bits();
+template <> __device__ __forceinline__ constexpr unsigned overflow_bits<_Float16>() { return 0x477FF000u; }
+template <> __device__ __forceinline__ constexpr unsigned overflow_bits<__bf16>() { return 0x7F7F8000u; }
+template <> __device__ __forceinline__ constexpr unsigned overflow_bits<float>() { return 0x7F800000u; }
+
 template <typename T, typename TO, bool SYM, bool CIN, int NW, int PITCH, typename ACC>
 __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                   int tm, int tn, int wm, int wn, int lane, int tid) {
@@ -521,12 +529,15 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
             if (!(grow + r < p.Mv && gcol + c < p.Nv)) v[r][c] = 0.f;
       }
       if (chk) {
+        // v is 0 outside the valid corner, so the block's largest |v| decides:
+        // cvt<TO>(v) is non-finite iff |v| (as fp32 bits, NaN above +inf)
+        // reaches TO's overflow threshold (the first value that rounds to inf)
+        unsigned m = 0;
 #pragma unroll
         for (int r = 0; r < 8; ++r)
 #pragma unroll
-          for (int c = 0; c < 8; ++c)
-            if (full || (grow + r < p.Mv && gcol + c < p.Nv))
-              finite = finite && __builtin_isfinite((float)cvt<TO>(v[r][c]));
+          for (int c = 0; c < 8; ++c) m = max(m, __builtin_bit_cast(unsigned, v[r][c]) & 0x7FFFFFFFu);
+        finite = finite && m < overflow_bits<TO>();
       }
       // 0: off the diagonal or below it; 1: on it; 2: above it
       const int cls = !diag_tile ? 0 : (grow >= gcol + 8 ? 0 : (grow == gcol ? 1 : 2));

@@ -93,7 +93,7 @@ int main(int argc, char **argv) {
       EXPECT(ns_muon_update(nullptr, idt, dummy, odt, n, 0.01, 0.0, 1.0, 1, 1, 1, nullptr) != NSG_OK);
       EXPECT(nsg_gemm_nt(idt, (int32_t)(rng() % 2), G, R, C, R, nullptr, R, (int32_t)(rng() % 3), nullptr, R,
                          (int32_t)(rng() % 3), 1.f, 0.f, nullptr, R, nullptr, C, nullptr, R, nullptr, 0.f, 0,
-                         nullptr) != NSG_OK);
+                         nullptr, nullptr) != NSG_OK);
     }
     (void)ns_status_string((nsg_status_t)pick({-1, 0, 1, 2, 3, 4, 5, 6, 1000}));
   }

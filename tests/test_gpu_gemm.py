@@ -167,3 +167,31 @@ def test_kmajor_rejected_where_unsupported():
         nsg.gemm_nt(A, A, tile=128, b_kmajor=True)
     with pytest.raises(nsg.NSGError):   # fp32
         nsg.gemm_nt(A.float(), A.float(), tile=256, b_kmajor=True)
+
+
+@pytest.mark.parametrize("dtype,big,ok", [(torch.float16, 65520.0, 65504.0),
+                                          (torch.bfloat16, float.fromhex("0x1.ffp127"), float.fromhex("0x1.fep127"))])
+@pytest.mark.parametrize("tile", [256])
+def test_nonfinite_flag_at_the_rounding_threshold(dtype, big, ok, tile):
+    """The status flag reports an output that is non-finite after rounding to
+    the output dtype: the fp16 (bf16) overflow threshold 65520 (0x1.ffp127,
+    halfway above the largest bf16, a tie that rounds to the even infinity)
+    rounds to infinity, the largest finite values do not; NaN is reported."""
+    n, K = 256, 256
+    A = torch.zeros(4, n, K, device="cuda", dtype=torch.float32)
+    A[:, 3, 5] = 1.0
+    B = torch.zeros(4, n, K, device="cuda", dtype=torch.float32)
+    B[:, 200, 5] = 1.0
+    vals = [ok, big, -big, float("nan")]
+    for g, v in enumerate(vals):
+        A[g, 3, 5] = 1.0 if v == v else float("nan")
+    st = torch.zeros(4, dtype=torch.int32, device="cuda")
+    # alpha carries the value in fp32: V[3, 200] = alpha * 1 * 1
+    outs = []
+    for g, v in enumerate(vals):
+        alpha = v if v == v else 1.0
+        o, _, _ = nsg.gemm_nt(A[g:g + 1].to(dtype), B[g:g + 1].to(dtype), alpha=alpha, tile=tile, status=st[g:g + 1])
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert st.tolist() == [0, 1, 1, 1]
+    assert torch.isfinite(outs[0].float()).all() and not torch.isfinite(outs[1].float()).all()
