@@ -372,7 +372,7 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
               safety=w.safety, compute_dtype=w.compute, sym_updates=sym_updates)
     ws = torch.empty(nsg.workspace_size(w.G, w.R, w.C, **kw), dtype=torch.uint8, device=dev)
     status = torch.zeros(w.G, dtype=torch.int32, device=dev)
-    plan = nsg.plan(w.R, w.C, **kw)
+    plan = nsg.plan(w.R, w.C, in_dtype=w.dtype, **kw)
     credited, executed = nsg.flops(w.R, w.C, **kw)
 
     if calibrate_copy:
@@ -446,9 +446,11 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), **common,
                     "algo_flops_per_launch": d["algo_flops"] / d["launches"]}
-    # normalize pass: reads the input twice (norm, then scale) and writes X0 once
-    in_bytes = x.numel() * x.element_size()
-    x0_bytes = w.G * w.n * w.m * (4 if w.compute == "f32" else 2)
+    # normalize pass: the norm reads the input; the scale pass reads it again
+    # and writes X0 once, or moves nothing when the products read the input in
+    # place (16-bit input in the compute dtype, sides multiples of 256)
+    norm_bytes = w.G * sum(e["bytes"] for e in plan if e["kind"] in (0, 1))
+    in_place = any(e["kind"] == 1 and e["label"] == "scales" for e in plan)
     norm_ms = sum(by_kernel.get(k, {"ms": 0})["ms"] for k in ("norm_reduce", "scale_cast_transpose"))
     kernels = {k: {"ms_per_step": round(v["ms"] / steps, 3),
                    "tflops_algo": round(v["algo_flops"] / (v["ms"] * 1e-3) / 1e12, 1) if v["algo_flops"] else None,
@@ -472,8 +474,8 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
                          "tflops": round(credited * hbm_roof_mps / 1e12, 1),
                          "frac": round(value / hbm_roof_mps, 4)},
         "normalize": {"ms_per_step": round(norm_ms / steps, 3),
-                      "algo_bytes": 2 * in_bytes + x0_bytes,
-                      "gbs": round((2 * in_bytes + x0_bytes) / (norm_ms / steps * 1e-3) / 1e9, 1) if norm_ms else None},
+                      "algo_bytes": norm_bytes, "input_read_in_place": in_place,
+                      "gbs": round(norm_bytes / (norm_ms / steps * 1e-3) / 1e9, 1) if norm_ms else None},
         "kernels": kernels,
         "roofline": roofline,
         "nonfinite_matrices": int(status.sum().item()),

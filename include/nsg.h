@@ -118,9 +118,15 @@ nsg_status_t ns_workspace_size(int64_t G, int64_t R, int64_t C,
 
 /* Orthogonalize a bucket.
  *   in      device, [G, R, C] row-major contiguous, dtype in_dtype; read only.
+ *           When in_dtype is the 16-bit compute dtype, R and C are multiples
+ *           of 256, `in` is 16-byte aligned and `out` does not overlap it,
+ *           the products read X0 = G 2^e straight from `in` (the exact power
+ *           of two rides in their fp32 epilogue scale) and no scaled copy is
+ *           written; the results are the same either way.
  *   out     device, [G, R, C] row-major contiguous, dtype out_dtype; may be
- *           the same memory as `in` (the input is fully consumed into the
- *           workspace before the first output write).
+ *           the same memory as `in` (the input is then fully consumed into
+ *           the workspace before the first output write); any other overlap
+ *           with `in` is an error the library does not detect.
  *   workspace  device, at least ns_workspace_size bytes, aligned to
  *           NSG_WORKSPACE_ALIGN; contents on entry are ignored and on exit
  *           undefined.
@@ -177,13 +183,14 @@ nsg_status_t ns_flops(int64_t R, int64_t C, const nsg_params_t *p,
 /* One entry of the launch plan (host only): what each kernel launch of a
  * call does, per matrix. */
 typedef struct {
-  int32_t kind;     /* 0 norm reduce, 1 scale/cast/transpose, 2 general GEMM,
+  int32_t kind;     /* 0 norm reduce, 1 scale/cast/transpose (scales only
+                       when the input is read in place), 2 general GEMM,
                        3 symmetric GEMM */
   int32_t step;     /* NS step t (1..T); 0 before the loop, T+1 for the output */
   int64_t M, N, K;  /* GEMM logical sizes (0 for the normalize kernels) */
   double flops;     /* executed FLOPs per matrix (tiles run, 2MNK per tile) */
-  double bytes;     /* algorithmic HBM bytes per matrix (16-bit input and
-                       output assumed): every distinct matrix the launch
+  double bytes;     /* algorithmic HBM bytes per matrix (16-bit output
+                       assumed): every distinct matrix the launch
                        reads, once (an operand that is also the added term,
                        or a matrix and its transposed copy, count once), and
                        every matrix of the method it writes, once (transposed
@@ -194,8 +201,10 @@ typedef struct {
 } nsg_launch_info_t;
 
 /* Writes up to max_entries launch descriptions for one call on an R x C
- * bucket and the total count to *count (host only). */
-nsg_status_t ns_plan(int64_t R, int64_t C, const nsg_params_t *p,
+ * bucket with input dtype in_dtype and the total count to *count (host
+ * only).  The list is that of an aligned input that the output does not
+ * overlap; the number of launches never depends on the input. */
+nsg_status_t ns_plan(int64_t R, int64_t C, int32_t in_dtype, const nsg_params_t *p,
                      nsg_launch_info_t *entries, int32_t max_entries,
                      int32_t *count);
 

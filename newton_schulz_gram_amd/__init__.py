@@ -106,7 +106,7 @@ def lib() -> ctypes.CDLL:
     L.ns_status_string.restype = ctypes.c_char_p
     L.ns_flops.argtypes = [i64, i64, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     L.ns_flops.restype = i32
-    L.ns_plan.argtypes = [i64, i64, P, ctypes.POINTER(LaunchInfo), i32, ctypes.POINTER(i32)]
+    L.ns_plan.argtypes = [i64, i64, i32, P, ctypes.POINTER(LaunchInfo), i32, ctypes.POINTER(i32)]
     L.ns_plan.restype = i32
     L.ns_timing_enable.argtypes = [i32]
     L.ns_timing_enable.restype = i32
@@ -202,13 +202,15 @@ def flops(R: int, C: int, **kw):
     return cr.value, ex.value
 
 
-def plan(R: int, C: int, **kw):
-    """The launch list of one call, as a list of dicts (host only)."""
+def plan(R: int, C: int, in_dtype=None, **kw):
+    """The launch list of one call on an input of dtype `in_dtype` (default:
+    the compute dtype), as a list of dicts (host only)."""
     p, _keep = make_params(**kw)
+    idt = p.compute_dtype if in_dtype is None else _dtype_code(in_dtype)
     n = ctypes.c_int32(0)
-    _check(lib().ns_plan(R, C, ctypes.byref(p), None, 0, ctypes.byref(n)), "ns_plan")
+    _check(lib().ns_plan(R, C, idt, ctypes.byref(p), None, 0, ctypes.byref(n)), "ns_plan")
     arr = (LaunchInfo * max(1, n.value))()
-    _check(lib().ns_plan(R, C, ctypes.byref(p), arr, n.value, ctypes.byref(n)), "ns_plan")
+    _check(lib().ns_plan(R, C, idt, ctypes.byref(p), arr, n.value, ctypes.byref(n)), "ns_plan")
     return [dict(kind=e.kind, kernel=KIND_NAMES[e.kind], step=e.step, M=e.M, N=e.N, K=e.K,
                  flops=e.flops, bytes=e.bytes, label=e.label.decode(), a_kmajor=bool(e.a_kmajor),
                  b_kmajor=bool(e.b_kmajor)) for e in arr[:n.value]]

@@ -50,6 +50,7 @@ struct Launch {
   int at = 0, bt = 0;  // operand stored K-major (K x M / K x N)
   float alpha = 1.f, beta = 0.f, diag = 0.f;
   int gpow = 0;
+  int gexp = 0;  // an operand is the caller's input, read in place
   bool final_out = false;
   double flops = 0.0, bytes = 0.0;
 };
@@ -61,6 +62,11 @@ struct Plan {
   // one layout of X only (the input's own: X^T for tall inputs, X for wide
   // ones); the products that need the other read it K-major
   bool single = false;
+  // the products read the caller's input where they would read X0 (one
+  // layout, 16-bit input in the compute dtype, R and C multiples of kPad):
+  // the scale pass then only finds the scales and writes no copy
+  bool direct = false;
+  int in_dtype = NSG_F16;
   int T = 0;
   uint64_t restarts = 0;  // bit t-1: restart at the top of step t
   bool restart_at(int t) const { return t >= 1 && t <= 64 && ((restarts >> (t - 1)) & 1u); }
@@ -138,6 +144,7 @@ void add_gemm(Plan &P, bool sym, int step, const char *label, int A, int B, int 
   L.M = (int)M; L.N = (int)N; L.K = (int)K; L.Mv = (int)Mv; L.Nv = (int)Nv;
   L.alpha = (float)alpha; L.beta = (float)beta; L.diag = (float)diag;
   L.gpow = gpow;
+  L.gexp = (A == kInUser || B == kInUser || Cin == kInUser) ? 1 : 0;
   L.final_out = final_out;
   const int bm = tile_m(P.cfg);
   L.flops = sym ? 2.0 * sym_tiles(M, bm) * bm * bm * (double)K : 2.0 * (double)M * N * K;
@@ -150,7 +157,7 @@ void add_gemm(Plan &P, bool sym, int step, const char *label, int A, int B, int 
   // valid K: K of a GEMM over X's long side is m, else n
   const double Kv = (K == P.mp) ? (double)P.m : (double)P.n;
   auto matrix_of = [](int id) {
-    if (id == kX0T) return (int)kX0;
+    if (id == kX0T || id == kInUser) return (int)kX0;
     if (id == kX1T) return (int)kX1;
     if (id == kS5) return (int)kS4;
     return id;
@@ -166,7 +173,10 @@ void add_gemm(Plan &P, bool sym, int step, const char *label, int A, int B, int 
   P.launches.push_back(L);
 }
 
-nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, int out_dtype, Plan &P) {
+// in_dtype: the input's dtype; in_place_ok: the input may be read in place
+// (16-byte aligned, no overlap with the output).
+nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, int out_dtype, int in_dtype,
+                        bool in_place_ok, Plan &P) {
   P.R = R; P.C = C;
   P.tr = R > C;
   P.n = std::min(R, C);
@@ -183,6 +193,8 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
   }
   P.cfg = choose_cfg(P.np, P.mp, P.cdtype);
   P.single = (P.cfg == kTile256) && (P.cdtype != NSG_F32);
+  P.in_dtype = in_dtype;
+  P.direct = P.single && in_dtype == P.cdtype && in_place_ok && R % kPad == 0 && C % kPad == 0;
   // power-of-two range shift f ~ log2(sqrt(n)): keeps X0 = X/||X||_F and
   // R0 = X0 X0^T away from fp16 subnormals (X0 entries ~ 1/sqrt(nm)).
   P.fexp = (int)std::floor(std::log2((double)P.n) / 2.0);
@@ -211,11 +223,17 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
   P.used[kPartials] = P.used[kGScale] = true;
 
   {
-    Launch L; L.kind = 0; L.label = "norm_reduce"; L.bytes = (double)R * C * dtype_size(0); P.launches.push_back(L);
-    Launch S; S.kind = 1; S.label = "scale_cast_T"; S.bytes = 0; P.launches.push_back(S);
+    Launch L; L.kind = 0; L.label = "norm_reduce"; L.bytes = (double)R * C * dtype_size(in_dtype);
+    P.launches.push_back(L);
+    Launch S; S.kind = 1; S.label = P.direct ? "scales" : "scale_cast_T"; S.bytes = 0; P.launches.push_back(S);
   }
+  // the X0 buffers are reserved in every case (ping-pong and restart targets
+  // too), so the workspace size does not depend on the input
   if (P.single) P.used[P.tr ? kX0T : kX0] = true;
   else P.used[kX0] = P.used[kX0T] = true;
+  // where X0 is read from: the stored copy, or the input in place
+  const int X0s = P.direct && !P.tr ? (int)kInUser : (int)kX0;
+  const int X0Ts = P.direct && P.tr ? (int)kInUser : (int)kX0T;
   const int last = P.T + 1;
   const int OUT = kOutUser;
   const bool sgl = P.single, tr = P.tr;
@@ -223,7 +241,7 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
 
   if (!P.gram) {
     // Algorithm 1: A = X X^T ; B = b A + c A^2 ; X = a X + B X.
-    int X = kX0, XT = kX0T, Xn = kX1, XnT = kX1T;
+    int X = X0s, XT = X0Ts, Xn = kX1, XnT = kX1T;
     double xs = xs0;
     int xpow = 1;
     for (int t = 1; t <= P.T; ++t) {
@@ -254,6 +272,9 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
         }
         std::swap(X, Xn);
         std::swap(XT, XnT);
+        // the input is never written: its ping-pong partner is the X0 buffer
+        if (Xn == kInUser) Xn = kX0;
+        if (XnT == kInUser) XnT = kX0T;
       } else if (P.tr) {
         // X'^T = a X^T + X^T B (B exactly symmetric): NT with A = X^T, B = B
         add_gemm(P, false, last, "Yt=aXt+XtB", XT, kS1, XT, OUT, kNone, kNone, mp, np, np, m, n, xs,
@@ -271,18 +292,18 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     }
   } else {
     // Algorithm 3 with the implicit a*I form of Appendix B.2.3.
-    int Xb = kX0, XbT = kX0T;
+    int Xb = X0s, XbT = X0Ts;
     double xs = xs0;
     int xpow = 1;
     int Rb = kS0, Zb = kS1, Qcur = kNone, Qfree[2] = {kS2, kS3}, RZb = kS4, RZTb = kS5;
     const bool symu = p->sym_updates != 0;
     bool r_scaled = true;  // R_true = 2^-2f R_stored (only R0)
     if (sgl && tr) {
-      add_gemm(P, true, 0, "R0=XXt", kX0T, kX0T, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
+      add_gemm(P, true, 0, "R0=XXt", XbT, XbT, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
                false);
       kmajor(1, 1);
     } else {
-      add_gemm(P, true, 0, "R0=XXt", kX0, kX0, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
+      add_gemm(P, true, 0, "R0=XXt", Xb, Xb, kNone, Rb, kNone, kNone, np, np, mp, n, n, 1.0, 0.0, 0.0, 2,
                false);
     }
     for (int t = 1; t <= P.T; ++t) {
@@ -290,7 +311,7 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
       if (P.restart_at(t)) {
         // X <- Q X ; R <- X X^T ; Q <- I   (Alg. 3, "restart to stabilize");
         // repeated restarts alternate between the two X buffers
-        const int Xn = (Xb == kX1) ? kX0 : kX1, XnT = (Xb == kX1) ? kX0T : kX1T;
+        const int Xn = (Xb == kX1 || XbT == kX1T) ? kX0 : kX1, XnT = (Xb == kX1 || XbT == kX1T) ? kX0T : kX1T;
         if (sgl && tr) {  // X^T <- X^T Q^T, and R = X X^T from X^T read K-major
           add_gemm(P, false, t, "Xt=XtQt", XbT, Qcur, kNone, XnT, kNone, kNone, mp, np, np, m, n, xs, 0.0, 0.0,
                    xpow, false);
@@ -356,8 +377,9 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
     }
   }
   // the scale pass reads the input once and writes X0 once (its transposed
-  // copy is a layout choice)
-  P.launches[1].bytes = (double)R * C * dtype_size(0) + (double)n * m * dtype_size(P.cdtype);
+  // copy is a layout choice); reading the input in place, it moves nothing
+  P.launches[1].bytes =
+      P.direct ? 0.0 : (double)R * C * dtype_size(in_dtype) + (double)n * m * dtype_size(P.cdtype);
 
   // workspace layout
   size_t off = 0;
@@ -484,7 +506,7 @@ nsg_status_t ns_workspace_size(int64_t G, int64_t R, int64_t C, const nsg_params
     return NSG_OK;
   }
   Plan P;
-  st = build_plan(R, C, p, G, NSG_F16, P);
+  st = build_plan(R, C, p, G, NSG_F16, p->compute_dtype, true, P);
   if (st != NSG_OK) return st;
   *bytes = P.total;
   return NSG_OK;
@@ -501,7 +523,7 @@ nsg_status_t ns_flops(int64_t R, int64_t C, const nsg_params_t *p, double *credi
     return NSG_OK;
   }
   Plan P;
-  st = build_plan(R, C, p, 1, NSG_F16, P);
+  st = build_plan(R, C, p, 1, NSG_F16, p->compute_dtype, true, P);
   if (st != NSG_OK) return st;
   const double n = (double)P.n, m = (double)P.m, T = (double)P.T;
   double cr;
@@ -520,11 +542,12 @@ nsg_status_t ns_flops(int64_t R, int64_t C, const nsg_params_t *p, double *credi
   return NSG_OK;
 }
 
-nsg_status_t ns_plan(int64_t R, int64_t C, const nsg_params_t *p, nsg_launch_info_t *entries,
+nsg_status_t ns_plan(int64_t R, int64_t C, int32_t in_dtype, const nsg_params_t *p, nsg_launch_info_t *entries,
                      int32_t max_entries, int32_t *count) {
   if (count == nullptr || max_entries < 0 || (max_entries > 0 && entries == nullptr)) return NSG_ERR_INVALID_ARG;
   nsg_status_t st = validate_params(p);
   if (st != NSG_OK) return st;
+  if (!valid_dtype(in_dtype)) return NSG_ERR_UNSUPPORTED_DTYPE;
   st = validate_shape(1, R, C);
   if (st != NSG_OK) return st;
   if (R == 0 || C == 0) {
@@ -532,7 +555,7 @@ nsg_status_t ns_plan(int64_t R, int64_t C, const nsg_params_t *p, nsg_launch_inf
     return NSG_OK;
   }
   Plan P;
-  st = build_plan(R, C, p, 1, NSG_F16, P);
+  st = build_plan(R, C, p, 1, NSG_F16, in_dtype, true, P);
   if (st != NSG_OK) return st;
   *count = (int32_t)P.launches.size();
   for (int i = 0; i < (int)P.launches.size() && i < max_entries; ++i) {
@@ -563,7 +586,13 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
   if (G == 0 || R == 0 || C == 0) return NSG_OK;
   if (in == nullptr || out == nullptr) return NSG_ERR_INVALID_ARG;
   Plan P;
-  st = build_plan(R, C, p, G, out_dtype, P);
+  // the input is read in place only if it is 16-byte aligned and the output
+  // does not overlap it (out == in is allowed and then takes the copy)
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(in), o0 = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t i1 = i0 + (uintptr_t)(G * R * C) * dtype_size(in_dtype);
+  const uintptr_t o1 = o0 + (uintptr_t)(G * R * C) * dtype_size(out_dtype);
+  const bool in_place_ok = i0 % 16 == 0 && (o1 <= i0 || i1 <= o0);
+  st = build_plan(R, C, p, G, out_dtype, in_dtype, in_place_ok, P);
   if (st != NSG_OK) return st;
   if (workspace == nullptr || workspace_bytes < P.total ||
       (reinterpret_cast<uintptr_t>(workspace) % NSG_WORKSPACE_ALIGN) != 0)
@@ -572,6 +601,11 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char *ws = reinterpret_cast<char *>(workspace);
   auto ptr = [&](int id) -> void * { return id >= 0 ? ws + P.off[id] : nullptr; };
+  // operand addresses, row pitches and matrix strides; the input in place is
+  // [G][R][C], dense
+  auto src = [&](int id) -> const void * { return id == kInUser ? in : ptr(id); };
+  auto ld_of = [&](int id) -> int64_t { return id == kInUser ? C : P.ld[id]; };
+  auto stride_of = [&](int id) -> int64_t { return id == kInUser ? R * C : elem_stride(P, id); };
   const size_t es = dtype_size(P.cdtype);
   (void)es;
 
@@ -606,7 +640,7 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
       a.tr = P.tr ? 1 : 0;
       a.rows_p = (int32_t)(P.tr ? P.mp : P.np);
       a.cols_p = (int32_t)(P.tr ? P.np : P.mp);
-      a.same = P.tr ? ptr(kX0T) : ptr(kX0);
+      a.same = P.direct ? nullptr : (P.tr ? ptr(kX0T) : ptr(kX0));
       a.swap = P.single ? nullptr : (P.tr ? ptr(kX0) : ptr(kX0T));
       a.ld_same = P.tr ? P.ld[kX0T] : P.ld[kX0];
       a.s_same = elem_stride(P, P.tr ? kX0T : kX0);
@@ -621,10 +655,10 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
       err = launch_scale(a, s);
     } else {
       GemmArgs a;
-      a.A = ptr(L.A); a.lda = P.ld[L.A]; a.sA = elem_stride(P, L.A);
-      a.B = ptr(L.B); a.ldb = P.ld[L.B]; a.sB = elem_stride(P, L.B);
+      a.A = src(L.A); a.lda = ld_of(L.A); a.sA = stride_of(L.A);
+      a.B = src(L.B); a.ldb = ld_of(L.B); a.sB = stride_of(L.B);
       a.a_trans = L.at; a.b_trans = L.bt;
-      if (L.Cin >= 0) { a.Cin = ptr(L.Cin); a.ldc = P.ld[L.Cin]; a.sC = elem_stride(P, L.Cin); }
+      if (L.Cin != kNone) { a.Cin = src(L.Cin); a.ldc = ld_of(L.Cin); a.sC = stride_of(L.Cin); }
       if (L.out0 == kOutUser) {
         a.out0 = out;
         a.ld0 = C;  // the caller's [R, C] layout; final launches produce exactly that
@@ -643,6 +677,7 @@ nsg_status_t ns_orthogonalize(const void *in, int32_t in_dtype, void *out, int32
       a.alpha = L.alpha; a.beta = L.beta;
       a.gscale = reinterpret_cast<const float *>(ptr(kGScale));
       a.gpow = L.gpow;
+      a.gexp = L.gexp;
       a.batch = (int32_t)G;
       err = launch_gemm(P.cdtype, L.kind == 3, P.cfg, a, s);
     }

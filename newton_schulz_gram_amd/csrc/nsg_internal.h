@@ -19,10 +19,15 @@ constexpr int kPad = 256;
 // the reduction order of a matrix never depends on the bucket size.
 constexpr int64_t kNormChunk = 16384;
 
-enum BufferKind : int { kOutUser = -2, kNone = -1 };
+// kInUser: the caller's input read in place (16-bit input in the compute
+// dtype, both sides multiples of kPad)
+enum BufferKind : int { kInUser = -3, kOutUser = -2, kNone = -1 };
 
 // One batched GEMM launch: V = alpha' A B^T + beta' Cin, with
-// alpha' = alpha * gscale[b]^gpow and beta' = beta * gscale[b]^gpow.
+// alpha' = alpha * gscale[b]^gpow and beta' = beta * gscale[b]^gpow, both
+// times 2^(gpow e[b]) when gexp is set (e[b]: the int32 exponent stored after
+// the G scales; the operands are then the unscaled input G, and G 2^e is the
+// stored X0).
 // A is M x K (lda), B is N x K (ldb), Cin is M x N (ldc), all in the compute
 // dtype, batches `s*` elements apart.  M, N, K are padded sizes (multiples of
 // the tile); Mv x Nv is the valid corner.  a_trans / b_trans: the operand is
@@ -56,6 +61,7 @@ struct GemmArgs {
   float alpha = 1.f, beta = 0.f;
   const float *gscale = nullptr;
   int32_t gpow = 0;
+  int32_t gexp = 0;
   int32_t *status = nullptr;  // set to 1 for a batch with a non-finite out0 value
   int32_t batch = 0;
 };
@@ -81,7 +87,7 @@ struct ScaleArgs {
   int32_t fexp = 0;
   int32_t tr = 0;  // 1: input is m x n (R > C)
   int32_t rows_p = 0, cols_p = 0;  // padded dims of the input's own layout
-  void *same = nullptr;  // rows_p x cols_p, the input's layout
+  void *same = nullptr;  // rows_p x cols_p, the input's layout (null: scales only)
   void *swap = nullptr;  // cols_p x rows_p, transposed
   int64_t ld_same = 0, ld_swap = 0;  // row pitches (elements)
   int64_t s_same = 0, s_swap = 0;    // elements per matrix

@@ -84,15 +84,28 @@ template <typename T> struct V4 { typedef T type __attribute__((ext_vector_type(
 // workspace outputs always cover the padding.  Accumulator layout of a 32x32
 // MFMA tile: lane l, register r holds row 8 (r/4) + 4 (l/32) + r%4, column
 // l%32, so 4 consecutive registers are 4 consecutive rows of one column.
+// alpha' and beta' of matrix g: times r^gpow (r = gscale[g]), and times
+// 2^(gpow e) as well when the operands are the unscaled input (gexp).  The
+// power of two is exact, so reading G in place gives the same values as
+// reading the stored X0 = G 2^e.
+__device__ __forceinline__ void input_scales(const GemmArgs &p, int g, float &alpha, float &beta) {
+  if (p.gscale == nullptr || p.gpow <= 0) return;
+  const float sg = p.gscale[g];
+  const float sc = (p.gpow == 1) ? sg : sg * sg;
+  alpha *= sc;
+  beta *= sc;
+  if (p.gexp) {
+    const int k = p.gpow * reinterpret_cast<const int32_t *>(p.gscale + p.batch)[g];
+    alpha = ldexpf(alpha, k);
+    beta = ldexpf(beta, k);
+  }
+}
+
 template <typename T, typename TO, bool SYM, int TM, int TN>
 __device__ __forceinline__ void epilogue(const GemmArgs &p, const f32x16 (&acc)[TM][TN], int g, bool diag_tile,
                                          int row0, int col0, int lane) {
-  float sc = 1.f;
-  if (p.gscale != nullptr && p.gpow > 0) {
-    const float sg = p.gscale[g];
-    sc = (p.gpow == 1) ? sg : sg * sg;
-  }
-  const float alpha = p.alpha * sc, beta = p.beta * sc;
+  float alpha = p.alpha, beta = p.beta;
+  input_scales(p, g, alpha, beta);
   const T *cin = p.Cin ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
   TO *o0 = p.out0 ? reinterpret_cast<TO *>(p.out0) + (size_t)g * p.s0 : nullptr;
   T *o1 = p.out1 ? reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1 : nullptr;
@@ -455,12 +468,8 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   constexpr int NV = 8 / VT;                // 16-byte vectors of T per 8 elements
   typedef typename Vec16<T>::type vt_t;
   typedef typename Vec16<TO>::type vo_t;
-  float sc = 1.f;
-  if (p.gscale != nullptr && p.gpow > 0) {
-    const float sg = p.gscale[g];
-    sc = (p.gpow == 1) ? sg : sg * sg;
-  }
-  const float alpha = p.alpha * sc, beta = p.beta * sc;
+  float alpha = p.alpha, beta = p.beta;
+  input_scales(p, g, alpha, beta);
   const T *cin = CIN ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
   TO *o0 = p.out0 ? reinterpret_cast<TO *>(p.out0) + (size_t)g * p.s0 : nullptr;
   T *o1 = p.out1 ? reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1 : nullptr;
@@ -1463,6 +1472,7 @@ static void launch_scale_in(const ScaleArgs &a, dim3 grid, hipStream_t s) {
 hipError_t launch_scale(const ScaleArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   hipLaunchKernelGGL(scale_finalize_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
+  if (a.same == nullptr) return hipGetLastError();  // the products read the input in place
   dim3 grid((unsigned)(a.cols_p / 64), (unsigned)(a.rows_p / 64), (unsigned)a.batch);
   const size_t es = a.in_dtype == NSG_F32 ? 4 : 2;
   const bool vec = (reinterpret_cast<uintptr_t>(a.in) % 16 == 0) && ((size_t)a.C * es) % 16 == 0;

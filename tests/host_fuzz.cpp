@@ -63,7 +63,7 @@ int main(int argc, char **argv) {
     nsg_launch_info_t ents[80];
     int32_t cnt = -1;
     const int32_t maxe = (int32_t)(rng() % 81);
-    st = ns_plan(R, C, pp, ents, maxe, &cnt);
+    st = ns_plan(R, C, (int32_t)pick({-1, 0, 1, 2, 3}), pp, ents, maxe, &cnt);
     if (st == NSG_OK) EXPECT(cnt >= 0);  // the total; at most maxe entries written
     const int64_t k = pick({-1, 0, 1, 7, 256, 4096, 5000});
     const int32_t dim = (int32_t)pick({-2, -1, 0, 1, 2});

@@ -410,3 +410,77 @@ def test_several_restarts(steps, restarts):
     check(out, ref, "f16", f"restarts {restarts}")
     out32 = run(x, steps=steps, coeffs=coeffs, restarts=restarts, compute_dtype="f32", out_dtype=torch.float32)
     check(out32, ref, "f32", f"restarts {restarts} fp32")
+
+
+# ---------------------------------------------------------------------------
+# A 16-bit input in the compute dtype, with both sides multiples of 256 and an
+# output that does not overlap it, is read in place by the products (its
+# per-matrix power of two 2^e rides in their fp32 scale) instead of through a
+# scaled copy; out == in takes the copy.  Where the copy G 2^e is exact
+# (e >= 0: scaling up never rounds) and no entry is an fp16 subnormal, the two
+# routes give the same bits.  With subnormal entries they may differ in a few
+# last bits: the f16 MFMA's sums over subnormal operands are not exactly
+# invariant under a power-of-two scale (measured: about 1 output in 2000 of
+# an all-subnormal operand moves by an ulp, with the same worst error against
+# fp64 either way), so there both routes are held to the oracle instead.
+# ---------------------------------------------------------------------------
+
+IN_PLACE_CASES = [
+    # G, R, C, params
+    (4, 2048, 512, {}),                           # tall, Gram (MoE-like)
+    (3, 768, 3072, {}),                           # wide, Gram (GPT-2-like)
+    (2, 1024, 1024, {}),                          # square: standard NS
+    (2, 2048, 512, dict(mode="standard")),        # tall, standard
+    (2, 512, 1536, dict(mode="standard")),        # wide, standard
+    (2, 2048, 512, dict(restart_after=0)),        # no restart: the output product reads the input
+    (2, 512, 2048, dict(steps=1)),                # one step
+    (2, 512, 1024, dict(steps=8, restarts=[3, 5], coeffs=MIXED10[:15] + MIXED10[-9:])),
+]
+
+
+def normal_range_gaussian(G, R, C, sigma, seed):
+    """N(0, sigma^2) entries in fp16 with magnitudes below 2^-13 lifted to
+    2^-13, so that no entry (nor its copy scaled up) is an fp16 subnormal."""
+    x = custom(G, R, C, "f32", "gaussian", seed=seed) * sigma
+    tiny = 2.0 ** -13
+    x = torch.where(x.abs() < tiny, torch.where(x < 0, torch.full_like(x, -tiny), torch.full_like(x, tiny)), x)
+    return x.half()
+
+
+def both_routes(x, **kw):
+    """(read in place, through the scaled copy) outputs of one input."""
+    xc = x.cuda()
+    y = nsg.orthogonalize(xc, **kw)
+    x2 = xc.clone()
+    y2 = nsg.orthogonalize(x2, out=x2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(xc, x.cuda())  # the input is never written
+    return y, y2
+
+
+@pytest.mark.parametrize("case", range(len(IN_PLACE_CASES)))
+def test_input_read_in_place_matches_the_copy(case):
+    G, R, C, kw = IN_PLACE_CASES[case]
+    x = normal_range_gaussian(G, R, C, 1e-2, 60 + case)
+    assert [e["label"] for e in nsg.plan(R, C, in_dtype="f16", **kw)][1] == "scales"
+    y, y2 = both_routes(x, **kw)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), case
+    if case in (0, 1, 2):
+        check(y, oracle_of(x, mode=kw.get("mode", "gram")), "f16", f"in place {case}")
+
+
+@pytest.mark.parametrize("sigma,shape", [(1.0, (4, 2048, 512)), (1e-2, (4, 2048, 512)), (2e-5, (2, 2048, 512)),
+                                         (1e-3, (2, 768, 3072))])
+def test_input_read_in_place_with_subnormal_entries(sigma, shape):
+    """Gaussian inputs with fp16-subnormal entries (2e-5: most of them; 1.0:
+    the copy G 2^e, e < 0, rounds its smallest entries into subnormals):
+    both routes meet the oracle bars."""
+    x = (custom(*shape, "f32", "gaussian", seed=70) * sigma).half()
+    ref = oracle_of(x)
+    y, y2 = both_routes(x)
+    rel, _ = check(y, ref, "f16", f"in place, sigma {sigma}")
+    rel2, _ = check(y2, ref, "f16", f"copy, sigma {sigma}")
+    d = (y.float() - y2.float()).norm() / y2.float().norm()
+    record(f"in place vs copy, {shape} N(0,{sigma}^2)", {"in_place_rel_max": float(rel.max()),
+                                                         "copy_rel_max": float(rel2.max()),
+                                                         "routes_rel_diff": float(d)})

@@ -127,7 +127,7 @@ def test_square_gram_falls_back_to_standard():
 def test_gram_plan_structure():
     """Alg. 3: R0, then per step Z (+Q for a fresh Q), Q update, RZ and R; the
     restart (X=QX, R=XX^T) at the top of step 3; R_2 and R_5 skipped; 18 GEMMs."""
-    P = nsg.plan(11008, 4096)
+    P = nsg.plan(11008, 4096, in_dtype="bf16")
     labels = [e["label"] for e in P]
     gemms = [e for e in P if e["kernel"].startswith("gemm")]
     assert len(gemms) == 18
@@ -350,3 +350,29 @@ def test_single_layout_plan():
     x_bytes = m * (n + 64) * es
     assert nsg.workspace_size(1, 11008, 4096) < 2 * x_bytes + 6 * n * (n + 64) * es
     assert nsg.workspace_size(1, 11008, 4096, compute_dtype="f32") > 4 * m * n * 4
+
+
+def test_in_place_plan():
+    """A 16-bit input in the compute dtype with both sides multiples of 256 is
+    read in place: the scale pass only finds the scales and writes no copy
+    (no bytes), the launches and the other entries are unchanged, and so is
+    the workspace.  A bf16 input with fp16 compute, a ragged side, fp32
+    compute and the 128 x 128 path (n < 512) keep the copy."""
+    def desc(P):
+        return [(e["label"], e["kernel"], e["flops"], e["a_kmajor"], e["b_kmajor"]) for e in P]
+    for R, C, kw in ((2048, 512, {}), (768, 3072, {}), (4096, 4096, {}), (2048, 512, dict(mode="standard")),
+                     (512, 1024, dict(steps=8, restarts=[3, 5]))):
+        direct = nsg.plan(R, C, in_dtype="f16", **kw)
+        copy = nsg.plan(R, C, in_dtype="bf16", **kw)
+        assert direct[1]["label"] == "scales" and direct[1]["bytes"] == 0
+        assert copy[1]["label"] == "scale_cast_T"
+        assert copy[1]["bytes"] == R * C * 2 + R * C * 2
+        assert desc(direct)[2:] == desc(copy)[2:]
+        assert [e["bytes"] for e in direct[2:]] == [e["bytes"] for e in copy[2:]]
+    # the norm reads the input in its own dtype
+    assert nsg.plan(2048, 512, in_dtype="f32")[0]["bytes"] == 2048 * 512 * 4
+    for R, C, kw in ((2000, 512, {}), (768, 3000, {}), (2048, 512, dict(compute_dtype="f32")), (2048, 256, {}),
+                     (256, 1024, {})):
+        assert nsg.plan(R, C, in_dtype=kw.get("compute_dtype", "f16"), **kw)[1]["label"] == "scale_cast_T"
+    with pytest.raises(nsg.NSGError):
+        nsg.plan(2048, 512, in_dtype=7)
