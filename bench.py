@@ -9,7 +9,9 @@ GEMM of Algorithm 3 or 1, output), inputs resident in HBM.  Prints one JSON
 line: matrices/s (whole job), effective TFLOP/s from the pages' FLOP formula
 and its fraction of the fp16 dense MFMA peak, a roofline object for the
 dominant kernel (per-launch durations from HIP events recorded by the library
-on the stream its kernels run on), the fp64 CPU oracle timed on a bounded
+on the stream its kernels run on, over K more calls timed right after the K
+throughput calls, which carry no per-launch events), the fp64 CPU oracle
+timed on a bounded
 sample of the same workload, a parity object comparing the GPU output with
 those oracle outputs, and (default workload only) the same figures for the
 other four buckets under "other_configs", each against the roofline that
@@ -387,8 +389,9 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
         nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
     torch.cuda.synchronize()
 
-    nsg.timing_enable(True)
-    nsg.timing_collect()
+    # timed region: `steps` whole calls, one event between calls and none
+    # inside them (the library's per-launch events add a marker pair to every
+    # launch: ~6 us each, 10% of a GPT-2-sized call)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -399,6 +402,16 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+
+    # per-launch durations: `steps` more calls with a HIP event pair around
+    # every launch, recorded by the library on the stream its kernels run on
+    nsg.timing_enable(True)
+    nsg.timing_collect()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
+    torch.cuda.synchronize()
+    wall_instrumented = time.perf_counter() - t1
     recs = nsg.timing_collect()
     nsg.timing_enable(False)
 
@@ -465,6 +478,7 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
         "ms_per_step": round(1e3 * wall / steps, 3),
         "ms_per_call_median": round(per_call[len(per_call) // 2], 3),
         "ms_per_call_iqr": round(per_call[(3 * len(per_call)) // 4] - per_call[len(per_call) // 4], 3),
+        "ms_per_call_instrumented": round(1e3 * wall_instrumented / steps, 3),
         "effective_tflops": round(eff_tflops, 2),
         "pct_fp16_peak": round(100 * eff_tflops / PEAK_FP16_TFLOPS, 2),
         "executed_tflops": round(executed * w.G * steps / wall / 1e12, 2),
