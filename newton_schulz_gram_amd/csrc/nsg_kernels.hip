@@ -672,16 +672,23 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs &p, const ACC &ac
 // then work on neighbouring tiles of the same matrix, whose operands stay in
 // the shared last-level cache, while each XCD's 32 tiles share operand panels
 // in its own L2.  (Giving each XCD whole matrices instead measured slower: the
-// shared last-level-cache hits are lost.)  The tail that does not fill a round
-// keeps the identity map.
+// shared last-level-cache hits are lost.)  The rem < 256 tiles of a last,
+// partial round (all of a launch smaller than one round) are split the same
+// way into 8 runs, one per XCD, as long as the XCD's share of those
+// workgroups: XCD x has q + (x < r) of them (q = rem / 8, r = rem % 8), so its
+// run starts at x q + min(x, r).  Neighbouring tiles then share an XCD's L2 in
+// a partial round too (a launch of 42 matrices of 3 x 3 tiles: 252 tiles).
 template <bool SYM>
 __device__ __forceinline__ void tile_256(const GemmArgs &p, unsigned L, unsigned total, int &g, int &tm, int &tn) {
   constexpr unsigned CH = 32, ROUND = 8 * CH;
   const unsigned full = total / ROUND;
-  unsigned V = L;
+  unsigned V;
+  const unsigned xcd = L & 7u, slot = L >> 3;
   if (L < full * ROUND) {
-    const unsigned xcd = L & 7u, slot = L >> 3;
     V = (slot / CH) * ROUND + xcd * CH + (slot % CH);
+  } else {
+    const unsigned rem = total - full * ROUND, q = rem >> 3, r = rem & 7u;
+    V = full * ROUND + xcd * q + min(xcd, r) + (slot % CH);
   }
   const int tiles_m = p.M >> 8, tiles_n = p.N >> 8;
   const int tiles = SYM ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
