@@ -122,6 +122,46 @@ def test_tile_schedule_covers_every_tile(dtype, kind, batch, n):
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_several_tiles_per_workgroup_with_cin_and_kmajor(dtype):
+    """Launches with more tiles than CUs (each workgroup runs several tiles,
+    loading the next tile's first stage during an epilogue): a symmetric
+    product with Cin and the +diag second store (40 x 10 tiles), and a general
+    product with a K-major B and Cin (12 x 24 tiles), every 256 x 256 block
+    against the fp32 reference and the K-major one bit for bit against the
+    row-major one."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    b, n, K = 40, 1024, 512
+    A = torch.randn(b, n, K, device="cuda", generator=g).to(dtype)
+    C = torch.randn(b, n, n, device="cuda", generator=g)
+    C = (C + C.transpose(1, 2)).to(dtype)
+    out, _, out_d = nsg.gemm_nt(A, A, alpha=0.5, beta=-0.25, Cin=C, symmetric=True, diag=1.5, tile=256)
+    torch.cuda.synchronize()
+    ref = ref_nt(A, A, 0.5, -0.25, C)
+    d = (out.float() - ref).view(b, n // 256, 256, n // 256, 256).norm(dim=(2, 4))
+    r = ref.view(b, n // 256, 256, n // 256, 256).norm(dim=(2, 4))
+    assert float((d / r).max()) <= 4 * TOL[dtype]
+    # the second store is v + 1.5 I rounded once: off the diagonal it equals
+    # the first, on it the fp32 reference plus 1.5
+    eye = torch.eye(n, device="cuda", dtype=torch.bool).unsqueeze(0).expand(b, n, n)
+    assert torch.equal(out_d[~eye], out[~eye])
+    dref = torch.diagonal(ref, dim1=1, dim2=2) + 1.5
+    assert rel(torch.diagonal(out_d, dim1=1, dim2=2), dref) <= TOL[dtype]
+    M, N = 768, 2048
+    A2 = torch.randn(12, M, K, device="cuda", generator=g).to(dtype)
+    B2 = torch.randn(12, N, K, device="cuda", generator=g).to(dtype)
+    C2 = torch.randn(12, M, N, device="cuda", generator=g).to(dtype)
+    o_row, _, _ = nsg.gemm_nt(A2, B2, alpha=2.0, beta=0.5, Cin=C2, tile=256)
+    o_km, _, _ = nsg.gemm_nt(A2, B2.transpose(1, 2).contiguous(), alpha=2.0, beta=0.5, Cin=C2, tile=256,
+                             b_kmajor=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_row, o_km)
+    ref2 = ref_nt(A2, B2, 2.0, 0.5, C2)
+    d2 = (o_row.float() - ref2).view(12, M // 256, 256, N // 256, 256).norm(dim=(2, 4))
+    r2 = ref2.view(12, M // 256, 256, N // 256, 256).norm(dim=(2, 4))
+    assert float((d2 / r2).max()) <= 4 * TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("n,K,batch", [(512, 768, 3), (1024, 2048, 2), (4352, 512, 1)])
 def test_kmajor_symmetric_gram_matches_row_major(dtype, n, K, batch):
     """X X^T with X passed K-major (as X^T, K x n): the transposed LDS reads
