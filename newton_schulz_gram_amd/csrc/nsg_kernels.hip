@@ -378,12 +378,17 @@ constexpr int kStages256 = 2;
 // stages between a prefetched slice and its direct load
 constexpr int kPrefetchAhead = 2;
 
-// 16-byte vector of 8 16-bit values, or of 4 floats.
-// Output stores of the GEMM epilogues are non-temporal: the tiles are not
-// read again by this kernel, and streaming them past the caches keeps the
-// shader clock up (cached stores of whole output tiles measured about 45%
-// slower on the general 4096 x 4096 products).
-template <typename V> __device__ __forceinline__ void st_stream(const V &v, V *p) { __builtin_nontemporal_store(v, p); }
+// Epilogue stores (16-byte vectors of 8 16-bit values, or of 4 floats).
+// General products stream their output tiles past the caches (non-temporal
+// stores; cached ones measured about 45% slower on the general 4096 x 4096
+// products of an earlier epilogue).  Symmetric products, which store each
+// block to two places, use plain stores: with the non-temporal hint their
+// epilogues took 16-22% more cycles per tile (calls: GPT-2-small bucket 2.9%
+// and MoE bucket 1.3% slower, the others unchanged).
+template <bool SYM, typename V> __device__ __forceinline__ void st_out(const V &v, V *p) {
+  if constexpr (SYM) *p = v;
+  else __builtin_nontemporal_store(v, p);
+}
 
 template <typename TO> struct Vec16 { typedef TO type __attribute__((ext_vector_type(16 / sizeof(TO)))); };
 
@@ -565,7 +570,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
                 vo_t w;
 #pragma unroll
                 for (int q = 0; q < VO; ++q) w[q] = cvt<TO>(v[r][e * VO + q]);
-                st_stream(w, reinterpret_cast<vo_t *>(b0 + (size_t)r * p.ld0 + e * VO));
+                st_out<SYM>(w, reinterpret_cast<vo_t *>(b0 + (size_t)r * p.ld0 + e * VO));
               }
           } else {
 #pragma unroll
@@ -573,7 +578,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
 #pragma unroll
               for (int c = 0; c < 8; ++c)
                 if (pad0 || (grow + r < p.Mv && gcol + c < p.Nv))
-                  st_stream(cvt<TO>(v[r][c]), b0 + (size_t)r * p.ld0 + c);
+                  st_out<SYM>(cvt<TO>(v[r][c]), b0 + (size_t)r * p.ld0 + c);
           }
         }
         if (o2 != nullptr) {
@@ -584,7 +589,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
               vt_t w;
 #pragma unroll
               for (int q = 0; q < VT; ++q) w[q] = cvt<T>(v[r][e * VT + q]);
-              st_stream(w, reinterpret_cast<vt_t *>(b2r + (size_t)r * p.ld2 + e * VT));
+              st_out<SYM>(w, reinterpret_cast<vt_t *>(b2r + (size_t)r * p.ld2 + e * VT));
             }
         }
         if (ot != nullptr) {  // columns: the transposed copy (and out2's mirror)
@@ -595,8 +600,8 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
               vt_t w;
 #pragma unroll
               for (int q = 0; q < VT; ++q) w[q] = cvt<T>(v[e * VT + q][c]);
-              st_stream(w, reinterpret_cast<vt_t *>(bt + (size_t)c * ldt + e * VT));
-              if (o2 != nullptr) st_stream(w, reinterpret_cast<vt_t *>(b2c + (size_t)c * p.ld2 + e * VT));
+              st_out<SYM>(w, reinterpret_cast<vt_t *>(bt + (size_t)c * ldt + e * VT));
+              if (o2 != nullptr) st_out<SYM>(w, reinterpret_cast<vt_t *>(b2c + (size_t)c * p.ld2 + e * VT));
             }
         }
       } else if (cls == 1) {
@@ -619,7 +624,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
                 vo_t x;
 #pragma unroll
                 for (int q = 0; q < VO; ++q) x[q] = cvt<TO>(w[r][e * VO + q]);
-                st_stream(x, reinterpret_cast<vo_t *>(b0 + (size_t)r * p.ld0 + e * VO));
+                st_out<SYM>(x, reinterpret_cast<vo_t *>(b0 + (size_t)r * p.ld0 + e * VO));
               }
           } else {
 #pragma unroll
@@ -627,7 +632,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
 #pragma unroll
               for (int c = 0; c < 8; ++c)
                 if (pad0 || (grow + r < p.Mv && gcol + c < p.Nv))
-                  st_stream(cvt<TO>(w[r][c]), b0 + (size_t)r * p.ld0 + c);
+                  st_out<SYM>(cvt<TO>(w[r][c]), b0 + (size_t)r * p.ld0 + c);
           }
         }
         if (o2 != nullptr) {  // + diag on the valid diagonal
@@ -638,7 +643,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
             for (int c = 0; c < 8; ++c)
               x[c / VT][c % VT] = cvt<T>((r == c && grow + r < p.Mv) ? w[r][c] + p.diag : w[r][c]);
 #pragma unroll
-            for (int e = 0; e < NV; ++e) st_stream(x[e], reinterpret_cast<vt_t *>(b2r + (size_t)r * p.ld2 + e * VT));
+            for (int e = 0; e < NV; ++e) st_out<SYM>(x[e], reinterpret_cast<vt_t *>(b2r + (size_t)r * p.ld2 + e * VT));
           }
         }
       }
