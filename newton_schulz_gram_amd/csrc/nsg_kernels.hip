@@ -455,6 +455,23 @@ __device__ __forceinline__ void stage_acc(const f32x4 (&acc)[8][TN], float *lds,
           make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
 }
 
+// Column passes (256 x 256 kernel): pass P stages every row of the tile for
+// columns 64 P .. 64 P + 63 of each wave column (wn 128 + ...), so all four
+// waves write a quarter (their column blocks 4 P .. 4 P + 3) at once.  Staged
+// column s = 64 wn + 16 jj + lane % 16 holds rows 0..255, rotated modulo 256.
+template <int PITCH, int P>
+__device__ __forceinline__ void stage_acc_cols(const f32x4 (&acc)[8][8], float *lds, int wm, int wn, int lane) {
+  const int sw = stage_rot(lane);  // the low 4 bits of the staged column are lane % 16
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 &a = acc[i][4 * P + jj];
+      *reinterpret_cast<float4 *>(lds + (wn * 64 + jj * 16 + (lane & 15)) * PITCH +
+                                  ((wm * 128 + i * 16 + 4 * (lane >> 4) + sw) & 255)) = make_float4(a[0], a[1], a[2], a[3]);
+    }
+}
+
 // Bits of the smallest positive fp32 value that rounds (to nearest even) to
 // infinity in TO: 65520 for fp16, 0x1.FFp127 for bf16 (halfway above the
 // largest bf16, and a tie rounds to the even infinity), +inf for fp32.
@@ -463,11 +480,13 @@ template <> __device__ __forceinline__ constexpr unsigned overflow_bits<_Float16
 template <> __device__ __forceinline__ constexpr unsigned overflow_bits<__bf16>() { return 0x7F7F8000u; }
 template <> __device__ __forceinline__ constexpr unsigned overflow_bits<float>() { return 0x7F800000u; }
 
-template <typename T, typename TO, bool SYM, bool CIN, int NW, int PITCH, typename ACC>
+template <typename T, typename TO, bool SYM, bool CIN, int NW, int PITCH, bool CP, typename ACC>
 __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                   int tm, int tn, int wm, int wn, int lane, int tid) {
   static_assert(PITCH % 4 == 0, "16-byte staging writes");
   static_assert(NW == 4, "two 8 x 8 blocks per thread and pass");
+  constexpr int SR = CP ? 256 : 128;  // staged rows (a power of two)
+  static_assert(PITCH >= SR + 4, "one staged column per PITCH floats");
   constexpr int VT = 16 / (int)sizeof(T);   // elements of T per 16 bytes
   constexpr int VO = 16 / (int)sizeof(TO);  // elements of TO per 16 bytes
   constexpr int NV = 8 / VT;                // 16-byte vectors of T per 8 elements
@@ -490,38 +509,43 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   const int rb = lane & 7, cb = lane >> 3;
   bool finite = true;
   vt_t cinv[2][8][NV];  // Cin of the thread's block it of a pass
+  // region reg of a pass: rows and columns of the tile it covers
+  auto reg_row = [&](int pass, int reg) { return CP ? (reg & 3) * 64 : pass * 128 + (reg & 1) * 64; };
+  auto reg_col = [&](int pass, int reg) { return CP ? (reg >> 2) * 128 + pass * 64 : (reg >> 1) * 64; };
   auto load_cin = [&](int pass, int it) {
     const int reg = wave + 4 * it;
-    const T *cp = cin + (size_t)(tm * 256 + pass * 128 + (reg & 1) * 64 + 8 * rb) * p.ldc +
-                  (tn * 256 + (reg >> 1) * 64 + 8 * cb);
+    const T *cp = cin + (size_t)(tm * 256 + reg_row(pass, reg) + 8 * rb) * p.ldc + (tn * 256 + reg_col(pass, reg) + 8 * cb);
 #pragma unroll
     for (int r = 0; r < 8; ++r)
 #pragma unroll
       for (int e = 0; e < NV; ++e) cinv[it][r][e] = *reinterpret_cast<const vt_t *>(cp + (size_t)r * p.ldc + e * VT);
   };
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int grow0 = tm * 256 + pass * 128;  // global row of staged row 0
-    const int gcol0 = tn * 256;
+  auto run_pass = [&](auto pass_c) {
+    const int pass = pass_c;
     if constexpr (CIN) load_cin(pass, 0);
     // ---- A: accumulators -> LDS ----
-    if (wm == pass) stage_acc<PITCH>(acc, lds, wn, lane);
+    if constexpr (CP) {
+      stage_acc_cols<PITCH, decltype(pass_c)::value>(acc, lds, wm, wn, lane);
+    } else {
+      if (wm == pass) stage_acc<PITCH>(acc, lds, wn, lane);
+    }
     __syncthreads();
     // ---- B: 8 x 8 blocks ----
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       if constexpr (CIN) { if (it == 0) load_cin(pass, 1); }
       const int reg = wave + 4 * it;
-      const int rr = (reg & 1) * 64 + 8 * rb, cc = (reg >> 1) * 64 + 8 * cb;
-      const int grow = grow0 + rr, gcol = gcol0 + cc;
+      // staged row rr and column cc of the block, and its place in the output
+      const int rr = (CP ? (reg & 3) * 64 : (reg & 1) * 64) + 8 * rb, cc = (reg >> (CP ? 2 : 1)) * 64 + 8 * cb;
+      const int grow = tm * 256 + reg_row(pass, reg) + 8 * rb, gcol = tn * 256 + reg_col(pass, reg) + 8 * cb;
       const bool full = grow + 8 <= p.Mv && gcol + 8 <= p.Nv;  // every element of the block is valid
       float v[8][8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const float *src = lds + (cc + c) * PITCH;
         const int rot = (cb & 1) ? ((c & 1) ? -4 : 4) : 0;  // stage_rot(cc + c)
-        const float4 x0 = *reinterpret_cast<const float4 *>(src + ((rr + rot) & 127));
-        const float4 x1 = *reinterpret_cast<const float4 *>(src + ((rr + 4 + rot) & 127));
+        const float4 x0 = *reinterpret_cast<const float4 *>(src + ((rr + rot) & (SR - 1)));
+        const float4 x1 = *reinterpret_cast<const float4 *>(src + ((rr + 4 + rot) & (SR - 1)));
         v[0][c] = x0.x; v[1][c] = x0.y; v[2][c] = x0.z; v[3][c] = x0.w;
         v[4][c] = x1.x; v[5][c] = x1.y; v[6][c] = x1.z; v[7][c] = x1.w;
       }
@@ -650,22 +674,29 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
       __builtin_amdgcn_sched_barrier(0);
     }
     if (pass == 0) __syncthreads();  // LDS is rewritten by the next pass
+  };
+  if constexpr (CP) {  // compile-time passes: their staging reads fixed accumulator columns
+    run_pass(std::integral_constant<int, 0>{});
+    run_pass(std::integral_constant<int, 1>{});
+  } else {  // a run-time loop (unrolled, the symmetric epilogues spill)
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) run_pass(pass);
   }
   if (chk && __ballot(!finite) != 0 && lane == 0) p.status[g] = 1;
 }
 
-template <typename T, bool SYM, bool CIN, int NW, int PITCH, typename ACC>
+template <typename T, bool SYM, bool CIN, int NW, int PITCH, bool CP = false, typename ACC>
 __device__ __forceinline__ void staged_epilogue(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                 int tm, int tn, int wm, int wn, int lane, int tid) {
   if constexpr (SYM) {
-    staged_epilogue_t<T, T, true, CIN, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+    staged_epilogue_t<T, T, true, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   } else {
     if (p.out0_dtype == NSG_F16)
-      staged_epilogue_t<T, _Float16, false, CIN, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, _Float16, false, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
     else if (p.out0_dtype == NSG_BF16)
-      staged_epilogue_t<T, __bf16, false, CIN, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, __bf16, false, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
     else
-      staged_epilogue_t<T, float, false, CIN, NW, PITCH>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, float, false, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   }
 }
 
@@ -975,10 +1006,15 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   constexpr int SLICE = 256 * 128;   // bytes of one operand slice
   constexpr int STAGE = 2 * SLICE;   // A slice then B slice
   constexpr int NLD = 8;             // 1 KB direct loads per operand per wave per stage
-  constexpr int EPI_PITCH = 132;
-  constexpr int EPI_BYTES = 256 * EPI_PITCH * 4;
+  // the epilogue stages 256 columns of 128 rows per pass (symmetric
+  // products) or 128 columns of 256 rows (general ones), 4 floats of padding
+  // per column
+  constexpr int EPI_COLS = SYM ? 256 : 128;
+  constexpr int EPI_PITCH = SYM ? 132 : 260;
+  constexpr int EPI_BYTES = EPI_COLS * EPI_PITCH * 4;
   constexpr int LDS_BYTES = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
+  static_assert(EPI_PITCH >= 256 * 128 / EPI_COLS + 4 && EPI_BYTES <= LDS_BYTES, "staging fits the LDS array");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1140,7 +1176,11 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
     }
 
   __syncthreads();  // all waves are done with the operand stages
-  staged_epilogue<T, SYM, CIN, NW, EPI_PITCH>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane, tid);
+  // general products stage column halves (all four waves at once), symmetric
+  // ones row halves (measured: -0.5 to -3% per general launch, while column
+  // passes slowed the symmetric ones)
+  staged_epilogue<T, SYM, CIN, NW, EPI_PITCH, !SYM>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane,
+                                                    tid);
   __syncthreads();  // the staging area is read before the next tile's loads overwrite it
   }
 }
