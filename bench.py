@@ -471,6 +471,13 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
                for k, v in by_kernel.items()}
     # whole call against the HBM roofline of its algorithmic bytes
     hbm_roof_mps = PEAK_HBM_GBS * 1e9 / bytes_per_matrix
+    x0_copy_roofline = None
+    if in_place:
+        es_in = x.element_size()
+        x0_bytes = bytes_per_matrix + w.R * w.C * es_in + w.n * w.m * (4 if w.compute == "f32" else 2)
+        x0_mps = PEAK_HBM_GBS * 1e9 / x0_bytes
+        x0_copy_roofline = {"bytes_per_matrix": x0_bytes, "matrices_per_s": round(x0_mps, 1),
+                            "frac": round(value / x0_mps, 4)}
     res = {
         "metric": label,
         "value": round(value, 3),
@@ -486,7 +493,11 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
         "algo_bytes_per_matrix": bytes_per_matrix,
         "hbm_roofline": {"matrices_per_s": round(hbm_roof_mps, 1),
                          "tflops": round(credited * hbm_roof_mps / 1e12, 1),
-                         "frac": round(value / hbm_roof_mps, 4)},
+                         "frac": round(value / hbm_roof_mps, 4),
+                         # the same count with the normalized X0 written once
+                         # and read back (the method's normalize step taken
+                         # literally), for a run that reads the input in place
+                         "with_x0_copy": x0_copy_roofline},
         "normalize": {"ms_per_step": round(norm_ms / steps, 3),
                       "algo_bytes": norm_bytes, "input_read_in_place": in_place,
                       "gbs": round(norm_bytes / (norm_ms / steps * 1e-3) / 1e9, 1) if norm_ms else None},
