@@ -469,6 +469,19 @@ def test_input_read_in_place_matches_the_copy(case):
         check(y, oracle_of(x, mode=kw.get("mode", "gram")), "f16", f"in place {case}")
 
 
+def test_input_read_in_place_bf16():
+    """bf16 input with bf16 compute is read in place too (bf16 has fp32's
+    exponent range, so the copy G 2^e is exact for N(0,1) entries): same bits
+    as the copy route, tall and wide, and within the oracle's bars."""
+    for case, (G, R, C) in enumerate(((3, 2048, 512), (2, 512, 1536))):
+        x = custom(G, R, C, "bf16", "gaussian", seed=80 + case)
+        kw = dict(compute_dtype="bf16")
+        assert [e["label"] for e in nsg.plan(R, C, in_dtype="bf16", **kw)][1] == "scales"
+        y, y2 = both_routes(x, **kw)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), case
+        check(y, oracle_of(x), "bf16", f"in place bf16 {case}")
+
+
 @pytest.mark.parametrize("sigma,shape", [(1.0, (4, 2048, 512)), (1e-2, (4, 2048, 512)), (2e-5, (2, 2048, 512)),
                                          (1e-3, (2, 768, 3072))])
 def test_input_read_in_place_with_subnormal_entries(sigma, shape):
