@@ -61,6 +61,26 @@ def test_noalloc_matches_workspace_entry_point(kw):
         assert rel.max() <= 3e-2, rel
 
 
+def test_noalloc_with_the_input_read_in_place():
+    """fp16 buckets whose sides are multiples of 256 are read in place by the
+    products (no scaled copy in the scratch); two calls in a row, the second
+    smaller, each bit for bit equal to the workspace entry point."""
+    first = custom(4, 768, 2048, "f16", "gaussian", seed=74).cuda()   # wide, Gram
+    second = custom(3, 2048, 512, "f16", "gaussian", seed=75).cuda()  # tall, Gram
+    for x in (first, second):
+        assert [e["label"] for e in nsg.plan(x.shape[1], x.shape[2], in_dtype="f16")][1] == "scales"
+        assert nsg.workspace_size(*x.shape) <= nsg.NOALLOC_MAX_BYTES
+    refs = [_with_workspace(x) for x in (first, second)]
+    torch.cuda.synchronize()
+    for x, ref in zip((first, second), refs):
+        out = torch.full_like(x, float("nan"))
+        st = torch.full((x.shape[0],), 7, dtype=torch.int32, device="cuda")
+        _noalloc(x, out, st)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert st.tolist() == [0] * x.shape[0]
+
+
 def test_noalloc_binding_and_oversize():
     x = custom(3, 256, 1024, "bf16", "gaussian", seed=73).cuda()
     out = torch.empty_like(x)
