@@ -123,6 +123,16 @@ nsg_status_t ns_workspace_size(int64_t G, int64_t R, int64_t C,
  *           the products read X0 = G 2^e straight from `in` (the exact power
  *           of two rides in their fp32 epilogue scale) and no scaled copy is
  *           written; the results are the same either way.
+ *           Under the same conditions a bf16 input with fp16 compute in Gram
+ *           mode with 512 <= min(R, C) < 2048 is read in place too (larger
+ *           buckets are bound by the MFMAs and keep the copy, which is then
+ *           faster): the products that read X0
+ *           convert the bf16 values to the fp16 X0 the copy would hold, and
+ *           R0 = X0 X0^T multiplies the bf16 values themselves (their
+ *           products are exact in fp32, so R0 is at least as accurate as from
+ *           the fp16 copy; entries of X0 below fp16's normal range keep their
+ *           bits).  A matrix with |G|_F outside about [2^-24, 2^49] takes a
+ *           scaled bf16 copy for R0 instead.
  *   out     device, [G, R, C] row-major contiguous, dtype out_dtype; may be
  *           the same memory as `in` (the input is then fully consumed into
  *           the workspace before the first output write); any other overlap
@@ -198,6 +208,12 @@ typedef struct {
   char label[24];   /* e.g. "R0=XXt", "Z", "Q=QZ+aQ", "RZ", "R=Z.RZ", "Y=QX" */
   int32_t a_kmajor; /* 1: A is read from a K-major buffer (K x M), else M x K */
   int32_t b_kmajor; /* 1: B is read from a K-major buffer (K x N), else N x K */
+  int32_t source;   /* where a GEMM's operands come from: 0 the compute dtype
+                       (workspace, or the input in place); for a bf16 input
+                       under fp16 compute read in place, 1 (2): A (B) is the
+                       input, converted to fp16 X0 = RNE(G 2^e) on its way to
+                       LDS; 3: a symmetric product of the raw bf16 input on
+                       bf16 MFMAs (fp32 accumulation) with fp16 outputs */
 } nsg_launch_info_t;
 
 /* Writes up to max_entries launch descriptions for one call on an R x C

@@ -70,7 +70,12 @@ class LaunchInfo(ctypes.Structure):
         ("label", ctypes.c_char * 24),
         ("a_kmajor", ctypes.c_int32),
         ("b_kmajor", ctypes.c_int32),
+        ("source", ctypes.c_int32),
     ]
+
+
+# nsg_launch_info_t.source: where a GEMM's operands come from
+SOURCE_NAMES = {0: "plain", 1: "A converted from bf16", 2: "B converted from bf16", 3: "raw bf16"}
 
 
 EXPORTS = ("ns_default_params", "ns_workspace_size", "ns_orthogonalize", "ns_status_string",
@@ -213,7 +218,7 @@ def plan(R: int, C: int, in_dtype=None, **kw):
     _check(lib().ns_plan(R, C, idt, ctypes.byref(p), arr, n.value, ctypes.byref(n)), "ns_plan")
     return [dict(kind=e.kind, kernel=KIND_NAMES[e.kind], step=e.step, M=e.M, N=e.N, K=e.K,
                  flops=e.flops, bytes=e.bytes, label=e.label.decode(), a_kmajor=bool(e.a_kmajor),
-                 b_kmajor=bool(e.b_kmajor)) for e in arr[:n.value]]
+                 b_kmajor=bool(e.b_kmajor), source=e.source) for e in arr[:n.value]]
 
 
 def nbytes(t: torch.Tensor) -> int:

@@ -19,9 +19,29 @@ constexpr int kPad = 256;
 // the reduction order of a matrix never depends on the bucket size.
 constexpr int64_t kNormChunk = 16384;
 
-// kInUser: the caller's input read in place (16-bit input in the compute
-// dtype, both sides multiples of kPad)
+// kInUser: the caller's input read in place (16-bit input, both sides
+// multiples of kPad; in the compute dtype, or bf16 under fp16 compute with the
+// operand sources below)
 enum BufferKind : int { kInUser = -3, kOutUser = -2, kNone = -1 };
+
+// Operand sources of the 16-bit 256 x 256 GEMM kernel.
+//   kSrcPlain: A and B in the kernel's dtype.
+//   kSrcCvtA / kSrcCvtB (fp16 kernel, general products): A (or B) is the
+//     caller's bf16 input; its K-slices are loaded raw into LDS and each wave
+//     converts the blocks it loaded to X_stored = RNE_fp16(x 2^e[b]), the
+//     value the scale pass would have stored, before the MFMAs read them.
+//   kSrcRaw (bf16 kernel, symmetric products, fp16 outputs): A = B = the
+//     caller's bf16 input G, whose products are exact in fp32, with alpha'
+//     times 2^(gpow e[b]), for every matrix whose exponent passes
+//     raw_exponent_ok(e[b]); any other matrix reads the bf16 copy G 2^e[b]
+//     at `fb` (ld `ldfb`, `sfb` elements per matrix) without that factor.
+enum OperandSource : int { kSrcPlain = 0, kSrcCvtA = 1, kSrcCvtB = 2, kSrcRaw = 3 };
+
+// Exponents e (X_stored = G 2^e) for which the symmetric product of the raw
+// bf16 input is safe: |G|_F ~ 2^(f - e) with f <= 8 then lies in
+// [2^-24, 2^49], so sums of products stay finite in fp32, every product of
+// entries above 2^-40 |G|_F stays a normal fp32 number, and 2^(2e) is one.
+__host__ __device__ constexpr bool raw_exponent_ok(int e) { return e >= -40 && e <= 24; }
 
 // One batched GEMM launch: V = alpha' A B^T + beta' Cin, with
 // alpha' = alpha * gscale[b]^gpow and beta' = beta * gscale[b]^gpow, both
@@ -62,6 +82,9 @@ struct GemmArgs {
   const float *gscale = nullptr;
   int32_t gpow = 0;
   int32_t gexp = 0;
+  int32_t src = kSrcPlain;  // OperandSource
+  const void *fb = nullptr;  // kSrcRaw: bf16 G 2^e of the matrices that fail raw_exponent_ok
+  int64_t ldfb = 0, sfb = 0;
   int32_t *status = nullptr;  // set to 1 for a batch with a non-finite out0 value
   int32_t batch = 0;
 };
@@ -91,7 +114,10 @@ struct ScaleArgs {
   void *swap = nullptr;  // cols_p x rows_p, transposed
   int64_t ld_same = 0, ld_swap = 0;  // row pitches (elements)
   int64_t s_same = 0, s_swap = 0;    // elements per matrix
-  int32_t cdtype = NSG_F16;
+  int32_t cdtype = NSG_F16;  // dtype of the copies
+  // 1: `same` (bf16 here) is written only for the matrices whose e fails
+  // raw_exponent_ok: the fallback operand of a kSrcRaw product
+  int32_t raw_fallback = 0;
   float *gscale = nullptr;   // [G] r, followed by [G] int32 e
   int32_t *status = nullptr;
   int32_t batch = 0;

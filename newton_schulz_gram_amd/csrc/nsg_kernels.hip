@@ -95,9 +95,10 @@ __device__ __forceinline__ void input_scales(const GemmArgs &p, int g, float &al
   alpha *= sc;
   beta *= sc;
   if (p.gexp) {
-    const int k = p.gpow * reinterpret_cast<const int32_t *>(p.gscale + p.batch)[g];
-    alpha = ldexpf(alpha, k);
-    beta = ldexpf(beta, k);
+    const int e = reinterpret_cast<const int32_t *>(p.gscale + p.batch)[g];
+    if (p.src == kSrcRaw && !raw_exponent_ok(e)) return;  // this matrix reads its scaled copy
+    alpha = ldexpf(alpha, p.gpow * e);
+    beta = ldexpf(beta, p.gpow * e);
   }
 }
 
@@ -496,9 +497,14 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   input_scales(p, g, alpha, beta);
   const T *cin = CIN ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
   TO *o0 = p.out0 ? reinterpret_cast<TO *>(p.out0) + (size_t)g * p.s0 : nullptr;
+  // the transposed copy and out2: TO for symmetric products (whose outputs
+  // all take one dtype), the compute dtype T for general ones
+  using TA = std::conditional_t<SYM, TO, T>;
+  static_assert(sizeof(TA) == sizeof(T), "16-byte vectors of TA hold VT elements");
+  typedef typename Vec16<TA>::type va_t;
   T *o1 = p.out1 ? reinterpret_cast<T *>(p.out1) + (size_t)g * p.s1 : nullptr;
-  T *o2 = (SYM && p.out2) ? reinterpret_cast<T *>(p.out2) + (size_t)g * p.s2 : nullptr;
-  T *ot = SYM ? reinterpret_cast<T *>(o0) : o1;  // transposed copy (symmetric outputs are in the compute dtype)
+  TA *o2 = (SYM && p.out2) ? reinterpret_cast<TA *>(p.out2) + (size_t)g * p.s2 : nullptr;
+  TA *ot = SYM ? reinterpret_cast<TA *>(o0) : reinterpret_cast<TA *>(o1);
   const int64_t ldt = SYM ? p.ld0 : p.ld1;
   const bool pad0 = p.out0_pad != 0;
   const bool chk = p.status != nullptr;
@@ -581,9 +587,9 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
       const int cls = !diag_tile ? 0 : (grow >= gcol + 8 ? 0 : (grow == gcol ? 1 : 2));
       // per-block bases; rows and columns step by uniform pitches
       TO *const b0 = o0 + (size_t)grow * p.ld0 + gcol;
-      T *const bt = ot + (size_t)gcol * ldt + grow;
-      T *const b2r = o2 + (size_t)grow * p.ld2 + gcol;
-      T *const b2c = o2 + (size_t)gcol * p.ld2 + grow;
+      TA *const bt = ot + (size_t)gcol * ldt + grow;
+      TA *const b2r = o2 + (size_t)grow * p.ld2 + gcol;
+      TA *const b2c = o2 + (size_t)gcol * p.ld2 + grow;
       if (cls == 0) {
         if (o0 != nullptr) {
           if (vec0 && full) {
@@ -610,10 +616,10 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
           for (int r = 0; r < 8; ++r)
 #pragma unroll
             for (int e = 0; e < NV; ++e) {
-              vt_t w;
+              va_t w;
 #pragma unroll
-              for (int q = 0; q < VT; ++q) w[q] = cvt<T>(v[r][e * VT + q]);
-              st_out<SYM>(w, reinterpret_cast<vt_t *>(b2r + (size_t)r * p.ld2 + e * VT));
+              for (int q = 0; q < VT; ++q) w[q] = cvt<TA>(v[r][e * VT + q]);
+              st_out<SYM>(w, reinterpret_cast<va_t *>(b2r + (size_t)r * p.ld2 + e * VT));
             }
         }
         if (ot != nullptr) {  // columns: the transposed copy (and out2's mirror)
@@ -621,11 +627,11 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
           for (int c = 0; c < 8; ++c)
 #pragma unroll
             for (int e = 0; e < NV; ++e) {
-              vt_t w;
+              va_t w;
 #pragma unroll
-              for (int q = 0; q < VT; ++q) w[q] = cvt<T>(v[e * VT + q][c]);
-              st_out<SYM>(w, reinterpret_cast<vt_t *>(bt + (size_t)c * ldt + e * VT));
-              if (o2 != nullptr) st_out<SYM>(w, reinterpret_cast<vt_t *>(b2c + (size_t)c * p.ld2 + e * VT));
+              for (int q = 0; q < VT; ++q) w[q] = cvt<TA>(v[e * VT + q][c]);
+              st_out<SYM>(w, reinterpret_cast<va_t *>(bt + (size_t)c * ldt + e * VT));
+              if (o2 != nullptr) st_out<SYM>(w, reinterpret_cast<va_t *>(b2c + (size_t)c * p.ld2 + e * VT));
             }
         }
       } else if (cls == 1) {
@@ -662,12 +668,12 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
         if (o2 != nullptr) {  // + diag on the valid diagonal
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            vt_t x[NV];
+            va_t x[NV];
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-              x[c / VT][c % VT] = cvt<T>((r == c && grow + r < p.Mv) ? w[r][c] + p.diag : w[r][c]);
+              x[c / VT][c % VT] = cvt<TA>((r == c && grow + r < p.Mv) ? w[r][c] + p.diag : w[r][c]);
 #pragma unroll
-            for (int e = 0; e < NV; ++e) st_out<SYM>(x[e], reinterpret_cast<vt_t *>(b2r + (size_t)r * p.ld2 + e * VT));
+            for (int e = 0; e < NV; ++e) st_out<SYM>(x[e], reinterpret_cast<va_t *>(b2r + (size_t)r * p.ld2 + e * VT));
           }
         }
       }
@@ -685,11 +691,13 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   if (chk && __ballot(!finite) != 0 && lane == 0) p.status[g] = 1;
 }
 
-template <typename T, bool SYM, bool CIN, int NW, int PITCH, bool CP = false, typename ACC>
+// TS: the dtype of a symmetric product's outputs (the compute dtype, or fp16
+// for the bf16-MFMA product of a raw bf16 input)
+template <typename T, bool SYM, bool CIN, int NW, int PITCH, bool CP = false, typename TS = T, typename ACC>
 __device__ __forceinline__ void staged_epilogue(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                 int tm, int tn, int wm, int wn, int lane, int tid) {
   if constexpr (SYM) {
-    staged_epilogue_t<T, T, true, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+    staged_epilogue_t<T, TS, true, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   } else {
     if (p.out0_dtype == NSG_F16)
       staged_epilogue_t<T, _Float16, false, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
@@ -996,25 +1004,55 @@ __device__ __forceinline__ F tr_frag(const unsigned char *p0, const unsigned cha
   return __builtin_bit_cast(F, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int DT, bool SYM, bool CIN, bool AT, bool BT>
+// bf16 pair -> fp16 pair, each RNE(x 2^e): the value the scale pass stores
+// for a bf16 input (bf16 -> fp32 is exact; ldexp and the conversion round once
+// each, as there).
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned w, int e) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const float lo = __builtin_bit_cast(float, w << 16), hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+  const h2 h = {(_Float16)ldexpf(lo, e), (_Float16)ldexpf(hi, e)};
+  return __builtin_bit_cast(unsigned, h);
+}
+
+// SRC (OperandSource): kSrcPlain; kSrcCvtA / kSrcCvtB, an operand converted
+// from the bf16 input in LDS (fp16 kernel, general products); kSrcRaw, the
+// symmetric product of the raw bf16 input on bf16 MFMAs with fp16 outputs.
+// Converted operand X: its 8 loads of a stage go to a raw area of LDS (one
+// slice, after the two stage slots) instead of the stage slot.  In step k,
+// the wave reads its own 1 KB block p of stage k + 1 from the raw area at H0
+// row p (each lane its own 16 bytes: no other wave touches them), converts
+// it into slot (k + 1) % 2 one row later (the read's latency hides behind
+// the row's MFMAs) and loads block p of stage k + 2 into the raw area again;
+// block 7 is written at H1 row 0, before barrier B.  The other operand's 8
+// loads are at H1 rows 1-4.  With 16 loads per stage, 15 were issued after
+// the one a read waits for, so every load has one step to land.
+template <int DT, bool SYM, bool CIN, bool AT, bool BT, int SRC = kSrcPlain>
 __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   using MF = Mfma16<DT>;
   using T = typename MF::T;
   using frag_t = typename MF::frag_t;
+  constexpr bool CVA = SRC == kSrcCvtA, CVB = SRC == kSrcCvtB, CV = CVA || CVB;
+  constexpr bool RAW = SRC == kSrcRaw;
+  static_assert(!CV || (DT == NSG_F16 && !SYM && !CIN), "converted operands: general fp16 products");
+  static_assert(!RAW || (DT == NSG_BF16 && SYM && !CIN && AT == BT), "raw input: symmetric bf16 products");
+  using TS = std::conditional_t<RAW, _Float16, T>;  // symmetric outputs
   constexpr int NW = 4;
   constexpr int BK = 64;             // K elements per stage (128-byte row slices)
   constexpr int SLICE = 256 * 128;   // bytes of one operand slice
   constexpr int STAGE = 2 * SLICE;   // A slice then B slice
   constexpr int NLD = 8;             // 1 KB direct loads per operand per wave per stage
+  constexpr int RAW_OFF = 2 * STAGE;  // converted operand: raw blocks of the next stage
+  constexpr int MAIN_BYTES = CV ? 2 * STAGE + SLICE : 2 * STAGE;
   // the epilogue stages 256 columns of 128 rows per pass (symmetric
   // products) or 128 columns of 256 rows (general ones), 4 floats of padding
   // per column
   constexpr int EPI_COLS = SYM ? 256 : 128;
   constexpr int EPI_PITCH = SYM ? 132 : 260;
   constexpr int EPI_BYTES = EPI_COLS * EPI_PITCH * 4;
-  constexpr int LDS_BYTES = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
+  constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
   static_assert(EPI_PITCH >= 256 * 128 / EPI_COLS + 4 && EPI_BYTES <= LDS_BYTES, "staging fits the LDS array");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1028,11 +1066,19 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   int g, tm, tn;
   tile_256<SYM>(p, L, total, g, tm, tn);
 
+  // exponent e[g] of the matrix (converted or raw operands)
+  const int ex = (CV || RAW) ? reinterpret_cast<const int32_t *>(p.gscale + p.batch)[g] : 0;
+  // operand bases and pitches: a raw product reads the input, or the scaled
+  // copy of a matrix outside raw_exponent_ok
+  const bool from_fb = RAW && !raw_exponent_ok(ex);
+  const void *baseA = from_fb ? p.fb : p.A, *baseB = from_fb ? p.fb : p.B;
+  const int64_t lda = from_fb ? p.ldfb : p.lda, ldb = from_fb ? p.ldfb : p.ldb;
+  const int64_t sA = from_fb ? p.sfb : p.sA, sB = from_fb ? p.sfb : p.sB;
   // direct-load sources: wave w fills the 1 KB blocks b = w + 4 i of each
   // slice (rows 8 b .. 8 b + 7; lane l writes chunk slot l % 8 of row
   // 8 b + l / 8, which holds logical chunk (l % 8) ^ ((row >> 1) & 7))
-  const T *gA = reinterpret_cast<const T *>(p.A) + (size_t)g * p.sA + (AT ? (size_t)tm * 256 : (size_t)tm * 256 * p.lda);
-  const T *gB = reinterpret_cast<const T *>(p.B) + (size_t)g * p.sB + (BT ? (size_t)tn * 256 : (size_t)tn * 256 * p.ldb);
+  const T *gA = reinterpret_cast<const T *>(baseA) + (size_t)g * sA + (AT ? (size_t)tm * 256 : (size_t)tm * 256 * lda);
+  const T *gB = reinterpret_cast<const T *>(baseB) + (size_t)g * sB + (BT ? (size_t)tn * 256 : (size_t)tn * 256 * ldb);
   // Per-lane offsets are rederived for every tile from a copy of the lane
   // index the compiler cannot see through, so they are never kept (and
   // spilled) across the epilogue.
@@ -1049,17 +1095,38 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   unsigned offA[NLD], offB[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    offA[i] = dma_off(AT, i, p.lda);
-    offB[i] = dma_off(BT, i, p.ldb);
+    offA[i] = dma_off(AT, i, lda);
+    offB[i] = dma_off(BT, i, ldb);
   }
   const int nk = p.K / BK;  // >= 4: K is a multiple of 256
   // stage kt of each operand: 64 K elements of every row, or 64 K-rows
-  const size_t stepA = AT ? (size_t)BK * p.lda : (size_t)BK, stepB = BT ? (size_t)BK * p.ldb : (size_t)BK;
+  const size_t stepA = AT ? (size_t)BK * lda : (size_t)BK, stepB = BT ? (size_t)BK * ldb : (size_t)BK;
   auto dma = [&](int kt, int slot, int q) {  // q-th of the 16 loads of a stage: pair q / 2, operand q % 2
     unsigned char *st = lds + slot * STAGE;
     const int i = q >> 1;
     if (q & 1) lds_dma16(gB + (size_t)kt * stepB, offB[i], st + SLICE + (wave + NW * i) * 1024);
     else lds_dma16(gA + (size_t)kt * stepA, offA[i], st + (wave + NW * i) * 1024);
+  };
+  // converted operand X (CV) and the other one, Y: block i of stage kt
+  auto x_load = [&](int kt, int i) {  // raw, into the raw area
+    if constexpr (CVA) lds_dma16(gA + (size_t)kt * stepA, offA[i], lds + RAW_OFF + (wave + NW * i) * 1024);
+    else lds_dma16(gB + (size_t)kt * stepB, offB[i], lds + RAW_OFF + (wave + NW * i) * 1024);
+  };
+  auto y_load = [&](int kt, int slot, int i) {
+    unsigned char *st = lds + slot * STAGE;
+    if constexpr (CVA) lds_dma16(gB + (size_t)kt * stepB, offB[i], st + SLICE + (wave + NW * i) * 1024);
+    else lds_dma16(gA + (size_t)kt * stepA, offA[i], st + (wave + NW * i) * 1024);
+  };
+  // this lane's 16 raw bytes of block i, and their conversion into X's
+  // slice of a slot
+  auto x_read = [&](int i) { return *reinterpret_cast<const uint4 *>(lds + RAW_OFF + (wave + NW * i) * 1024 + 16 * lane); };
+  auto x_write = [&](const uint4 &w, int slot, int i) {
+    uint4 r;
+    r.x = bf16x2_to_f16x2(w.x, ex);
+    r.y = bf16x2_to_f16x2(w.y, ex);
+    r.z = bf16x2_to_f16x2(w.z, ex);
+    r.w = bf16x2_to_f16x2(w.w, ex);
+    *reinterpret_cast<uint4 *>(lds + slot * STAGE + (CVA ? 0 : SLICE) + (wave + NW * i) * 1024 + 16 * lane) = r;
   };
 
   // fragment reads: lane l reads row (block row + l % 16), K elements
@@ -1107,11 +1174,35 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
     acc[i][j] = MF::mma(a[i][1], b[j][1], acc[i][j]);
   };
 
+  if constexpr (CV) {
+    // stage 0: X raw, Y; convert X (and load stage 1's raw X block by
+    // block); then Y of stage 1: the order of loads in a step
 #pragma unroll
-  for (int q = 0; q < 2 * NLD; ++q) dma(0, 0, q);
+    for (int i = 0; i < NLD; ++i) x_load(0, i);
 #pragma unroll
-  for (int q = 0; q < 2 * NLD; ++q) dma(1, 1, q);
-  wait_vmcnt<2 * NLD>();  // stage 0 landed
+    for (int i = 0; i < NLD; ++i) y_load(0, 0, i);
+    wait_vmcnt<NLD>();  // X of stage 0 landed
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 xr[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) xr[i] = x_read(i);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      x_write(xr[i], 0, i);
+      x_load(1, i);  // after its raw block was read
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) y_load(1, 1, i);
+    wait_vmcnt<2 * NLD>();  // Y of stage 0 landed
+    wait_lgkmcnt0();        // the converted X of stage 0 is written
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2 * NLD; ++q) dma(0, 0, q);
+#pragma unroll
+    for (int q = 0; q < 2 * NLD; ++q) dma(1, 1, q);
+    wait_vmcnt<2 * NLD>();  // stage 0 landed
+  }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 8; ++i) rd_a(lds, i);
@@ -1125,13 +1216,44 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
     const unsigned char *nst = lds + ((kt + 1) & 1) * STAGE;
     const int kn = kt + 2;
     const int dslot = kt & 1;
+    // CV, at H0 row xi (xi = 0..7) and H1 row 0 (xi = 8): the raw block
+    // xi - 1 of X of stage kt+1, read one row earlier, into slot
+    // (kt+1) % 2 and (REFILL) stage kt+2's raw block xi - 1 loaded; then
+    // block xi of stage kt+1 (15 loads were issued after it, stage kt+2's
+    // blocks 0 .. xi-1 among them with REFILL) read for the next row
+    uint4 xt;
+    auto x_step = [&](auto xi_c) {
+      constexpr int xi = decltype(xi_c)::value;
+      if constexpr (xi >= 1) {
+        x_write(xt, (kt + 1) & 1, xi - 1);
+        if (REFILL) x_load(kn, xi - 1);
+      }
+      if constexpr (xi < NLD) {
+        wait_vmcnt<REFILL ? 2 * NLD - 1 : 2 * NLD - 1 - xi>();
+        __builtin_amdgcn_sched_barrier(0);
+        xt = x_read(xi);
+      }
+    };
     // ---- H0: columns 0-3 ----
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         pair(i, j);
-        if (REFILL && i >= 1 && i <= 4 && (j & 1)) dma(kn, dslot, 2 * (i - 1) + (j >> 1));
+        if constexpr (CV) {
+          if (j == 1) {
+            if (i == 0) x_step(std::integral_constant<int, 0>{});
+            if (i == 1) x_step(std::integral_constant<int, 1>{});
+            if (i == 2) x_step(std::integral_constant<int, 2>{});
+            if (i == 3) x_step(std::integral_constant<int, 3>{});
+            if (i == 4) x_step(std::integral_constant<int, 4>{});
+            if (i == 5) x_step(std::integral_constant<int, 5>{});
+            if (i == 6) x_step(std::integral_constant<int, 6>{});
+            if (i == 7) x_step(std::integral_constant<int, 7>{});
+          }
+        } else {
+          if (REFILL && i >= 1 && i <= 4 && (j & 1)) dma(kn, dslot, 2 * (i - 1) + (j >> 1));
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (REFILL && i == 0) {
@@ -1147,7 +1269,12 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
 #pragma unroll
       for (int j = 4; j < 8; ++j) {
         pair(i, j);
-        if (REFILL && i >= 1 && i <= 4 && (j & 1)) dma(kn, dslot, 8 + 2 * (i - 1) + ((j - 4) >> 1));
+        if constexpr (CV) {
+          if (i == 0 && j == 5) x_step(std::integral_constant<int, 8>{});
+          if (REFILL && i >= 1 && i <= 4 && (j & 1)) y_load(kn, dslot, 2 * (i - 1) + ((j - 4) >> 1));
+        } else {
+          if (REFILL && i >= 1 && i <= 4 && (j & 1)) dma(kn, dslot, 8 + 2 * (i - 1) + ((j - 4) >> 1));
+        }
         if (i == 1) rd_b(nst, j - 4);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1156,6 +1283,7 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
         // of stage kt+2 issued in the first half may be in flight)
         if (REFILL) wait_vmcnt<8>();
         else wait_vmcnt<0>();
+        if constexpr (CV) wait_lgkmcnt0();  // the converted blocks of stage kt+1 are written
         raw_barrier();  // B: every wave's loads of stage kt+1 landed
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1179,8 +1307,8 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   // general products stage column halves (all four waves at once), symmetric
   // ones row halves (measured: -0.5 to -3% per general launch, while column
   // passes slowed the symmetric ones)
-  staged_epilogue<T, SYM, CIN, NW, EPI_PITCH, !SYM>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn, lane,
-                                                    tid);
+  staged_epilogue<T, SYM, CIN, NW, EPI_PITCH, !SYM, TS>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn,
+                                                        lane, tid);
   __syncthreads();  // the staging area is read before the next tile's loads overwrite it
   }
 }
@@ -1247,7 +1375,25 @@ static hipError_t launch_256(const GemmArgs &a, hipStream_t s) {
     if (a.a_trans != a.b_trans && (SYM || a.a_trans)) return hipErrorInvalidValue;
     const int mode = a.a_trans ? 2 : (a.b_trans ? 1 : 0);
 #define NSG_H(C, AT_, BT_) hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, C, AT_, BT_>), dim3(grid), dim3(256), 0, s, a)
-    if (a.Cin != nullptr) {
+#define NSG_HS(AT_, BT_, S_) \
+  hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, false, AT_, BT_, S_>), dim3(grid), dim3(256), 0, s, a)
+    if (a.src != kSrcPlain) {
+      // an operand from the caller's bf16 input: converted (general fp16
+      // products, X0 as A of a row-major pair or as the K-major B) or raw
+      // (symmetric bf16 products)
+      if (a.Cin != nullptr || a.gscale == nullptr) return hipErrorInvalidValue;
+      if constexpr (DT == NSG_F16 && !SYM) {
+        if (a.src == kSrcCvtA && mode == 0) NSG_HS(false, false, kSrcCvtA);
+        else if (a.src == kSrcCvtB && mode == 1) NSG_HS(false, true, kSrcCvtB);
+        else return hipErrorInvalidValue;
+      } else if constexpr (DT == NSG_BF16 && SYM) {
+        if (a.src != kSrcRaw || a.fb == nullptr || a.A != a.B || a.lda != a.ldb) return hipErrorInvalidValue;
+        if (mode == 0) NSG_HS(false, false, kSrcRaw);
+        else NSG_HS(true, true, kSrcRaw);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    } else if (a.Cin != nullptr) {
       if (mode == 0) NSG_H(true, false, false);
       else if (mode == 1) NSG_H(true, false, true);
       else NSG_H(true, true, true);
@@ -1257,6 +1403,7 @@ static hipError_t launch_256(const GemmArgs &a, hipStream_t s) {
       else NSG_H(false, true, true);
     }
 #undef NSG_H
+#undef NSG_HS
   }
   return hipGetLastError();
 }
@@ -1453,6 +1600,7 @@ __global__ void __launch_bounds__(256) scale_cast_transpose16_kernel(const Scale
   const int g = blockIdx.z;
   const int tid = threadIdx.x;
   const int e = reinterpret_cast<const int32_t *>(p.gscale + p.batch)[g];
+  if (p.raw_fallback && raw_exponent_ok(e)) return;  // the product reads this matrix raw
   const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 128;
   const TI *in = reinterpret_cast<const TI *>(p.in) + (size_t)g * (size_t)(p.R * p.C);
   TO *same = reinterpret_cast<TO *>(p.same) + (size_t)g * p.s_same;

@@ -482,6 +482,67 @@ def test_input_read_in_place_bf16():
         check(y, oracle_of(x), "bf16", f"in place bf16 {case}")
 
 
+BF16_IN_PLACE_CASES = [
+    # G, R, C, params
+    (4, 2048, 512, {}),                           # tall: R0 of the raw input read K-major, X^T Q^T converts A
+    (3, 768, 3072, {}),                           # wide: R0 row-major, Q X converts the K-major B
+    (2, 2048, 512, dict(restart_after=0)),        # no restart: the output product converts
+    (2, 512, 2048, dict(steps=1)),                # one step, wide
+    (2, 512, 1024, dict(steps=8, restarts=[3, 5], coeffs=MIXED10[:15] + MIXED10[-9:])),
+    (2, 1536, 512, dict(sym_updates=False)),      # general Q and RZ updates
+]
+
+
+@pytest.mark.parametrize("case", range(len(BF16_IN_PLACE_CASES)))
+def test_bf16_input_read_in_place_matches_the_copy(case):
+    """A bf16 input under fp16 compute read in place: R0 from the raw bf16
+    values on bf16 MFMAs, X0 converted on its way to LDS in the products that
+    read it.  On inputs whose X0 = G 2^e has no fp16-subnormal entry the bf16
+    values convert exactly, their products are the same in either MFMA, and
+    the output has the copy route's bits."""
+    G, R, C, kw = BF16_IN_PLACE_CASES[case]
+    x = normal_range_gaussian(G, R, C, 1e-2, 90 + case).bfloat16()
+    P = nsg.plan(R, C, in_dtype="bf16", **kw)
+    assert P[1]["label"] == "scales" and {e["source"] for e in P} == {0, 3, 1 if R > C else 2}
+    y, y2 = both_routes(x, **kw)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), case
+    if case < 2:
+        check(y, oracle_of(x.float()), "f16", f"bf16 in place {case}")
+
+
+@pytest.mark.parametrize("R,C", [(2048, 512), (512, 1536)])
+def test_bf16_input_outside_the_raw_range(R, C):
+    """Matrices scaled by 2^-40 and 2^60 (|G|_F near 2^-30 and 2^70) fall
+    outside the raw product's exponent window: the scale pass writes their
+    bf16 copy G 2^e, R0 reads it, and every matrix of the bucket (those read
+    raw too: scales 1 and 2^-20) keeps the copy route's bits."""
+    x = normal_range_gaussian(4, R, C, 1e-2, 95).float()
+    for b, k in enumerate((0, -40, 60, -20)):
+        x[b] *= 2.0 ** k
+    x = x.bfloat16()
+    y, y2 = both_routes(x)
+    for b in range(4):
+        assert torch.equal(y[b].view(torch.int16), y2[b].view(torch.int16)), b
+    check(y, oracle_of(x.float()), "f16", f"bf16 outside the raw range {R}x{C}")
+
+
+@pytest.mark.parametrize("sigma", [1.0, 1e-3])
+def test_bf16_input_read_in_place_gaussian(sigma):
+    """Gaussian bf16 inputs (X0 holds fp16-subnormal entries, which the raw
+    R0 keeps exact and the copy rounds): both routes meet the oracle bars and
+    stay within 2e-3 of each other (measured 7e-4: once one rounding differs,
+    the two runs part at the level of fp16's unit roundoff)."""
+    x = (custom(3, 2048, 512, "f32", "gaussian", seed=97) * sigma).bfloat16()
+    ref = oracle_of(x.float())
+    y, y2 = both_routes(x)
+    rel, _ = check(y, ref, "f16", f"bf16 in place, sigma {sigma}")
+    rel2, _ = check(y2, ref, "f16", f"bf16 copy, sigma {sigma}")
+    d = float((y.float() - y2.float()).norm() / y2.float().norm())
+    record(f"bf16 in place vs copy, N(0,{sigma}^2)", {"in_place_rel_max": float(rel.max()),
+                                                     "copy_rel_max": float(rel2.max()), "routes_rel_diff": d})
+    assert d < 2e-3
+
+
 @pytest.mark.parametrize("sigma,shape", [(1.0, (4, 2048, 512)), (1e-2, (4, 2048, 512)), (2e-5, (2, 2048, 512)),
                                          (1e-3, (2, 768, 3072))])
 def test_input_read_in_place_with_subnormal_entries(sigma, shape):

@@ -363,16 +363,47 @@ def test_in_place_plan():
     for R, C, kw in ((2048, 512, {}), (768, 3072, {}), (4096, 4096, {}), (2048, 512, dict(mode="standard")),
                      (512, 1024, dict(steps=8, restarts=[3, 5]))):
         direct = nsg.plan(R, C, in_dtype="f16", **kw)
-        copy = nsg.plan(R, C, in_dtype="bf16", **kw)
+        copy = nsg.plan(R, C, in_dtype="f32", **kw)
         assert direct[1]["label"] == "scales" and direct[1]["bytes"] == 0
         assert copy[1]["label"] == "scale_cast_T"
-        assert copy[1]["bytes"] == R * C * 2 + R * C * 2
+        assert copy[1]["bytes"] == R * C * 4 + R * C * 2
         assert desc(direct)[2:] == desc(copy)[2:]
         assert [e["bytes"] for e in direct[2:]] == [e["bytes"] for e in copy[2:]]
+        assert all(e["source"] == 0 for e in direct + copy)
     # the norm reads the input in its own dtype
     assert nsg.plan(2048, 512, in_dtype="f32")[0]["bytes"] == 2048 * 512 * 4
     for R, C, kw in ((2000, 512, {}), (768, 3000, {}), (2048, 512, dict(compute_dtype="f32")), (2048, 256, {}),
                      (256, 1024, {})):
         assert nsg.plan(R, C, in_dtype=kw.get("compute_dtype", "f16"), **kw)[1]["label"] == "scale_cast_T"
+        assert nsg.plan(R, C, in_dtype="bf16", **kw)[1]["label"] == "scale_cast_T"
     with pytest.raises(nsg.NSGError):
         nsg.plan(2048, 512, in_dtype=7)
+
+
+def test_bf16_input_plan():
+    """A bf16 input under fp16 compute in Gram mode, both sides multiples of
+    256, 512 <= n < 2048: the scale pass writes no copy, R0 = X0 X0^T
+    multiplies the raw bf16 input (source 3) and the general products that
+    read X0 convert it (source 1 for A, 2 for the K-major B); everything else
+    is the plan of an fp16 input.  Standard mode, square inputs and n >= 2048
+    keep the copy."""
+    def desc(P):
+        return [(e["label"], e["kernel"], e["flops"], e["a_kmajor"], e["b_kmajor"], e["bytes"]) for e in P]
+    for R, C, kw, x0_readers in (
+            (2048, 512, {}, {"R0=XXt": 3, "Xt=XtQt": 1}),
+            (768, 3072, {}, {"R0=XXt": 3, "X=QX": 2}),
+            (4096, 1536, {}, {"R0=XXt": 3, "Xt=XtQt": 1}),
+            (2048, 512, dict(restart_after=0), {"R0=XXt": 3, "Yt=XtQt": 1}),
+            (512, 2048, dict(steps=1), {"R0=XXt": 3, "Y=QX": 2}),
+            (512, 1024, dict(steps=8, restarts=[3, 5]), {"R0=XXt": 3, "X=QX": 2})):
+        P = nsg.plan(R, C, in_dtype="bf16", **kw)
+        assert P[1]["label"] == "scales" and P[1]["bytes"] == 0
+        sources = [(e["label"], e["source"]) for e in P if e["source"]]
+        # exactly the first launch of each X0 reader (a later restart reads X1)
+        assert dict(sources) == x0_readers and len(sources) == len(x0_readers), sources
+        assert desc(P)[2:] == desc(nsg.plan(R, C, in_dtype="f16", **kw))[2:]
+    for R, C, kw in ((4096, 4096, {}), (2048, 512, dict(mode="standard")), (2048, 512, dict(compute_dtype="bf16")),
+                     (2000, 512, {}), (256, 1024, {}), (11008, 4096, {}), (2048, 8192, {})):
+        P = nsg.plan(R, C, in_dtype="bf16", **kw)
+        assert all(e["source"] == 0 for e in P), (R, C, kw)
+        assert P[1]["label"] == ("scales" if kw.get("compute_dtype") == "bf16" else "scale_cast_T")
