@@ -34,10 +34,13 @@ def _replays_match(fn, ref, x, fresh, n=4):
         torch.matmul(torch.randn(64, 64, device="cuda"), torch.randn(64, 64, device="cuda"))  # eager work between
 
 
-@pytest.mark.parametrize("shape", [(1, 128, 512), (4, 768, 3072), (8, 2048, 512)])
-def test_graph_replay_orthogonalize(shape):
+@pytest.mark.parametrize("shape,dtype", [((1, 128, 512), "f16"), ((4, 768, 3072), "f16"), ((8, 2048, 512), "f16"),
+                                         ((4, 768, 3072), "bf16"), ((8, 2048, 512), "bf16")])
+def test_graph_replay_orthogonalize(shape, dtype):
+    """fp16 inputs read in place; bf16 ones (fp16 compute) read in place
+    through the raw R0 and the converting X = QX0."""
     G, R, C = shape
-    fresh = [custom(G, R, C, "f16", "gaussian", seed=60 + i).cuda() for i in range(2)]
+    fresh = [custom(G, R, C, dtype, "gaussian", seed=60 + i).cuda() for i in range(2)]
     x = fresh[0].clone()
     out = torch.empty_like(x)
     ws = torch.empty(nsg.workspace_size(G, R, C), dtype=torch.uint8, device="cuda")

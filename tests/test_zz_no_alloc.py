@@ -61,14 +61,20 @@ def test_noalloc_matches_workspace_entry_point(kw):
         assert rel.max() <= 3e-2, rel
 
 
-def test_noalloc_with_the_input_read_in_place():
-    """fp16 buckets whose sides are multiples of 256 are read in place by the
-    products (no scaled copy in the scratch); two calls in a row, the second
-    smaller, each bit for bit equal to the workspace entry point."""
-    first = custom(4, 768, 2048, "f16", "gaussian", seed=74).cuda()   # wide, Gram
-    second = custom(3, 2048, 512, "f16", "gaussian", seed=75).cuda()  # tall, Gram
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_noalloc_with_the_input_read_in_place(dtype):
+    """16-bit buckets whose sides are multiples of 256 are read in place by
+    the products (no scaled copy in the scratch; a bf16 input under fp16
+    compute through the raw R0 and the converting X = QX0, and one matrix of
+    the first bucket, scaled by 2^-40, through the bf16 copy the scale pass
+    writes into the scratch); two calls in a row, the second smaller, each bit
+    for bit equal to the workspace entry point."""
+    first = custom(4, 768, 2048, dtype, "gaussian", seed=74).cuda()   # wide, Gram
+    second = custom(3, 2048, 512, dtype, "gaussian", seed=75).cuda()  # tall, Gram
+    if dtype == "bf16":
+        first[1] *= 2.0 ** -40
     for x in (first, second):
-        assert [e["label"] for e in nsg.plan(x.shape[1], x.shape[2], in_dtype="f16")][1] == "scales"
+        assert [e["label"] for e in nsg.plan(x.shape[1], x.shape[2], in_dtype=dtype)][1] == "scales"
         assert nsg.workspace_size(*x.shape) <= nsg.NOALLOC_MAX_BYTES
     refs = [_with_workspace(x) for x in (first, second)]
     torch.cuda.synchronize()
