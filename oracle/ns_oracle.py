@@ -19,7 +19,7 @@ Every matrix product is ``numpy.matmul`` in float64; nothing is blocked, fused
 or reordered beyond what the algorithms state, so each line can be checked
 against the pages by eye.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * safety factor s: applied once, at normalization (X / (s (||X||_F + eps))).
     The per-polynomial form p(x/s) of Appendix B.2.2 equals this scaling
     applied at every step; it is obtained by passing rescaled coefficients.

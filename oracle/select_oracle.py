@@ -11,7 +11,7 @@ Rows may be replaced by columns; without sharding the pages select along the
 smaller dimension.  The update and error-feedback steps (5-10) are not part
 of this front-end.
 
-Readings (also listed in the design doc):
+Readings of points the pages leave open:
   * the l1 norms are exact sums of |M_ij| (math.fsum, correctly rounded), so
     the selection is fixed by the data alone;
   * equal norms are broken by the lower index; S is kept in ascending order

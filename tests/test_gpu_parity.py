@@ -77,13 +77,13 @@ def check(out, ref, compute, label=""):
 
 
 def record(label, stats):
-    """Print one line of measured errors (and keep it under gpurun_out/ when
-    that folder exists, for the design notes)."""
+    """Print one line of measured errors, and append it to
+    parity_errors.jsonl in the folder NSG_RECORD_DIR names, if it is set."""
     line = json.dumps({"case": label, **{k: (round(v, 7) if isinstance(v, float) else v)
                                          for k, v in stats.items()}})
     print(line, flush=True)
-    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
-    if os.path.isdir(d):
+    d = os.environ.get("NSG_RECORD_DIR")
+    if d and os.path.isdir(d):
         with open(os.path.join(d, "parity_errors.jsonl"), "a") as fh:
             fh.write(line + "\n")
 
