@@ -510,6 +510,26 @@ def test_bf16_input_read_in_place_matches_the_copy(case):
         check(y, oracle_of(x.float()), "f16", f"bf16 in place {case}")
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "f16"])
+def test_bf16_input_read_in_place_other_output_dtypes(out_dtype):
+    """fp32 and fp16 outputs of a bf16 input read in place, against the copy
+    route: a copy of the input 2 bytes past a 16-byte boundary is not read in
+    place (the products need 16-byte rows), so it takes the scaled copy."""
+    G, R, C = 3, 2048, 512
+    x = normal_range_gaussian(G, R, C, 1e-2, 98).bfloat16().cuda()
+    buf = torch.empty(G * R * C + 8, dtype=torch.bfloat16, device="cuda")
+    xm = buf[1:1 + G * R * C].view(G, R, C)
+    xm.copy_(x)
+    assert x.data_ptr() % 16 == 0 and xm.data_ptr() % 16 == 2
+    odt = {"f32": torch.float32, "f16": torch.float16}[out_dtype]
+    y = nsg.orthogonalize(x, out_dtype=odt)
+    y2 = nsg.orthogonalize(xm, out_dtype=odt)
+    torch.cuda.synchronize()
+    assert y.dtype == y2.dtype == odt
+    assert torch.equal(y, y2)
+    check(y, oracle_of(x.float().cpu()), "f16", f"bf16 in place, {out_dtype} output")
+
+
 @pytest.mark.parametrize("R,C", [(2048, 512), (512, 1536)])
 def test_bf16_input_outside_the_raw_range(R, C):
     """Matrices scaled by 2^-40 and 2^60 (|G|_F near 2^-30 and 2^70) fall
