@@ -1041,7 +1041,10 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   constexpr int SLICE = 256 * 128;   // bytes of one operand slice
   constexpr int STAGE = 2 * SLICE;   // A slice then B slice
   constexpr int NLD = 8;             // 1 KB direct loads per operand per wave per stage
-  constexpr int RAW_OFF = 2 * STAGE;  // converted operand: raw blocks of the next stage
+  // converted operand: raw blocks of the next stage.  The epilogue's staging
+  // area reaches into it; no raw load is in flight by then (the last raw
+  // blocks are converted in the step before the last stage).
+  constexpr int RAW_OFF = 2 * STAGE;
   constexpr int MAIN_BYTES = CV ? 2 * STAGE + SLICE : 2 * STAGE;
   // the epilogue stages 256 columns of 128 rows per pass (symmetric
   // products) or 128 columns of 256 rows (general ones), 4 floats of padding
