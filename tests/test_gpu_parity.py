@@ -530,6 +530,28 @@ def test_bf16_input_read_in_place_other_output_dtypes(out_dtype):
     check(y, oracle_of(x.float().cpu()), "f16", f"bf16 in place, {out_dtype} output")
 
 
+def test_bf16_input_read_in_place_degenerate_matrices():
+    """A zero matrix (its exponent leaves the raw window: R0 reads the zero
+    copy), one with a NaN and one with an infinity (read raw), next to a
+    normal one: the status flags of both routes agree, the zero and the
+    normal matrix keep the copy route's bits, the zero one's output is zero."""
+    G, R, C = 4, 2048, 512
+    x = normal_range_gaussian(G, R, C, 1e-2, 99).bfloat16().cuda()
+    x[0].zero_()
+    x[1, 5, 7] = float("nan")
+    x[2, 100, 3] = float("inf")
+    st = torch.full((G,), 7, dtype=torch.int32, device="cuda")
+    st2 = torch.full((G,), 7, dtype=torch.int32, device="cuda")
+    y = nsg.orthogonalize(x, status=st)
+    x2 = x.clone()
+    y2 = nsg.orthogonalize(x2, out=x2, status=st2)
+    torch.cuda.synchronize()
+    assert st.tolist() == st2.tolist() == [0, 1, 1, 0]
+    for b in (0, 3):
+        assert torch.equal(y[b].view(torch.int16), y2[b].view(torch.int16)), b
+    assert not torch.any(y[0] != 0)
+
+
 @pytest.mark.parametrize("R,C", [(2048, 512), (512, 1536)])
 def test_bf16_input_outside_the_raw_range(R, C):
     """Matrices scaled by 2^-40 and 2^60 (|G|_F near 2^-30 and 2^70) fall
