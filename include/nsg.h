@@ -131,8 +131,9 @@ nsg_status_t ns_workspace_size(int64_t G, int64_t R, int64_t C,
  *           R0 = X0 X0^T multiplies the bf16 values themselves (their
  *           products are exact in fp32, so R0 is at least as accurate as from
  *           the fp16 copy; entries of X0 below fp16's normal range keep their
- *           bits).  A matrix with |G|_F outside about [2^-24, 2^49] takes a
- *           scaled bf16 copy for R0 instead.
+ *           bits).  A matrix with |G|_F outside about [2^-20, 2^45] (where
+ *           fp32 sums of raw products could overflow or small products
+ *           flush) takes a scaled bf16 copy for R0 instead.
  *   out     device, [G, R, C] row-major contiguous, dtype out_dtype; may be
  *           the same memory as `in` (the input is then fully consumed into
  *           the workspace before the first output write); any other overlap
