@@ -67,11 +67,12 @@ struct Plan {
   // layout, 16-bit input in the compute dtype, R and C multiples of kPad):
   // the scale pass then only finds the scales and writes no copy
   bool direct = false;
-  // the same for a bf16 input under fp16 compute (Gram mode, n < 2048):
-  // R0 = X0 X0^T on bf16 MFMAs from the raw input, the general products that
-  // read X0 convert it on its way to LDS; the scale pass writes the bf16 copy
-  // G 2^e only for matrices whose exponent fails raw_exponent_ok (R0 reads
-  // those)
+  // the same for a bf16 input under fp16 compute (n < 2048): the first
+  // X X^T (R0, or the standard step's A) on bf16 MFMAs from the raw input,
+  // the general products that read X0 convert it on its way to LDS (and in
+  // their epilogue, where X0 is also the added term of X = a X + B X); the
+  // scale pass writes the bf16 copy G 2^e only for matrices whose exponent
+  // fails raw_exponent_ok (the first X X^T reads those)
   bool cvt = false;
   int in_dtype = NSG_F16;
   int T = 0;
@@ -202,11 +203,11 @@ nsg_status_t build_plan(int64_t R, int64_t C, const nsg_params_t *p, int64_t G, 
   P.single = (P.cfg == kTile256) && (P.cdtype != NSG_F32);
   P.in_dtype = in_dtype;
   P.direct = P.single && in_dtype == P.cdtype && in_place_ok && R % kPad == 0 && C % kPad == 0;
-  // Measured per call against the copy (bf16 N(0,1) inputs, same data): +3.2%
-  // at n = 512, +2.4% at 768, +1.5% at 1024, +0.3% at 1536, -0.4% at 2048,
-  // -1.7% at 3072 and 4096.  The conversion's VALU work and raw staging cost
-  // the compute-bound X = Q X0 of a large n more than the saved copy.
-  P.cvt = P.single && P.gram && in_dtype == NSG_BF16 && P.cdtype == NSG_F16 && in_place_ok && R % kPad == 0 &&
+  // Measured per Gram call against the copy (bf16 N(0,1) inputs, same data):
+  // +3.2% at n = 512, +2.4% at 768, +1.5% at 1024, +0.3% at 1536, -0.4% at
+  // 2048, -1.7% at 3072 and 4096.  The conversion's VALU work and raw staging
+  // cost the compute-bound X = Q X0 of a large n more than the saved copy.
+  P.cvt = P.single && in_dtype == NSG_BF16 && P.cdtype == NSG_F16 && in_place_ok && R % kPad == 0 &&
           C % kPad == 0 && P.n < 2048;
   // power-of-two range shift f ~ log2(sqrt(n)): keeps X0 = X/||X||_F and
   // R0 = X0 X0^T away from fp16 subnormals (X0 entries ~ 1/sqrt(nm)).

@@ -481,7 +481,9 @@ template <> __device__ __forceinline__ constexpr unsigned overflow_bits<_Float16
 template <> __device__ __forceinline__ constexpr unsigned overflow_bits<__bf16>() { return 0x7F7F8000u; }
 template <> __device__ __forceinline__ constexpr unsigned overflow_bits<float>() { return 0x7F800000u; }
 
-template <typename T, typename TO, bool SYM, bool CIN, int NW, int PITCH, bool CP, typename ACC>
+// CINB: Cin is the caller's bf16 input; each value enters as the fp16 X0 the
+// scale pass would store, RNE(x 2^e[g]).
+template <typename T, typename TO, bool SYM, bool CIN, int NW, int PITCH, bool CP, bool CINB, typename ACC>
 __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                   int tm, int tn, int wm, int wn, int lane, int tid) {
   static_assert(PITCH % 4 == 0, "16-byte staging writes");
@@ -496,6 +498,16 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
   float alpha = p.alpha, beta = p.beta;
   input_scales(p, g, alpha, beta);
   const T *cin = CIN ? reinterpret_cast<const T *>(p.Cin) + (size_t)g * p.sC : nullptr;
+  static_assert(!CINB || (CIN && sizeof(T) == 2), "a bf16 Cin replaces a 16-bit one");
+  const int cex = CINB ? reinterpret_cast<const int32_t *>(p.gscale + p.batch)[g] : 0;
+  auto cin_value = [&](T v) -> float {
+    if constexpr (CINB) {
+      const float x = __builtin_bit_cast(float, (unsigned)__builtin_bit_cast(unsigned short, v) << 16);
+      return (float)(_Float16)ldexpf(x, cex);
+    } else {
+      return (float)v;
+    }
+  };
   TO *o0 = p.out0 ? reinterpret_cast<TO *>(p.out0) + (size_t)g * p.s0 : nullptr;
   // the transposed copy and out2: TO for symmetric products (whose outputs
   // all take one dtype), the compute dtype T for general ones
@@ -562,7 +574,7 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
           // one fixed rounding: fma(beta', Cin, alpha' acc), whatever the
           // compiler would contract
           float x = alpha * v[r][c];
-          if constexpr (CIN) x = __builtin_fmaf(beta, (float)cinv[it][r][c / VT][c % VT], x);
+          if constexpr (CIN) x = __builtin_fmaf(beta, cin_value(cinv[it][r][c / VT][c % VT]), x);
           v[r][c] = x;
         }
       if (!full) {
@@ -693,18 +705,19 @@ __device__ __forceinline__ void staged_epilogue_t(const GemmArgs &p, const ACC &
 
 // TS: the dtype of a symmetric product's outputs (the compute dtype, or fp16
 // for the bf16-MFMA product of a raw bf16 input)
-template <typename T, bool SYM, bool CIN, int NW, int PITCH, bool CP = false, typename TS = T, typename ACC>
+template <typename T, bool SYM, bool CIN, int NW, int PITCH, bool CP = false, typename TS = T, bool CINB = false,
+          typename ACC>
 __device__ __forceinline__ void staged_epilogue(const GemmArgs &p, const ACC &acc, float *lds, int g,
                                                 int tm, int tn, int wm, int wn, int lane, int tid) {
   if constexpr (SYM) {
-    staged_epilogue_t<T, TS, true, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+    staged_epilogue_t<T, TS, true, CIN, NW, PITCH, CP, CINB>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   } else {
     if (p.out0_dtype == NSG_F16)
-      staged_epilogue_t<T, _Float16, false, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, _Float16, false, CIN, NW, PITCH, CP, CINB>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
     else if (p.out0_dtype == NSG_BF16)
-      staged_epilogue_t<T, __bf16, false, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, __bf16, false, CIN, NW, PITCH, CP, CINB>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
     else
-      staged_epilogue_t<T, float, false, CIN, NW, PITCH, CP>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
+      staged_epilogue_t<T, float, false, CIN, NW, PITCH, CP, CINB>(p, acc, lds, g, tm, tn, wm, wn, lane, tid);
   }
 }
 
@@ -1015,8 +1028,9 @@ __device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned w, int e) {
 }
 
 // SRC (OperandSource): kSrcPlain; kSrcCvtA / kSrcCvtB, an operand converted
-// from the bf16 input in LDS (fp16 kernel, general products); kSrcRaw, the
-// symmetric product of the raw bf16 input on bf16 MFMAs with fp16 outputs.
+// from the bf16 input in LDS (fp16 kernel, general products; a Cin term is
+// then that input too, converted in the epilogue); kSrcRaw, the symmetric
+// product of the raw bf16 input on bf16 MFMAs with fp16 outputs.
 // Converted operand X: its 8 loads of a stage go to a raw area of LDS (one
 // slice, after the two stage slots) instead of the stage slot.  In step k,
 // the wave reads its own 1 KB block p of stage k + 1 from the raw area at H0
@@ -1033,7 +1047,7 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   using frag_t = typename MF::frag_t;
   constexpr bool CVA = SRC == kSrcCvtA, CVB = SRC == kSrcCvtB, CV = CVA || CVB;
   constexpr bool RAW = SRC == kSrcRaw;
-  static_assert(!CV || (DT == NSG_F16 && !SYM && !CIN), "converted operands: general fp16 products");
+  static_assert(!CV || (DT == NSG_F16 && !SYM), "converted operands: general fp16 products");
   static_assert(!RAW || (DT == NSG_BF16 && SYM && !CIN && AT == BT), "raw input: symmetric bf16 products");
   using TS = std::conditional_t<RAW, _Float16, T>;  // symmetric outputs
   constexpr int NW = 4;
@@ -1310,8 +1324,9 @@ __global__ void __launch_bounds__(256, 1) gemm256h_kernel(const GemmArgs p) {
   // general products stage column halves (all four waves at once), symmetric
   // ones row halves (measured: -0.5 to -3% per general launch, while column
   // passes slowed the symmetric ones)
-  staged_epilogue<T, SYM, CIN, NW, EPI_PITCH, !SYM, TS>(p, acc, reinterpret_cast<float *>(lds), g, tm, tn, wm, wn,
-                                                        lane, tid);
+  // with a converted operand, a Cin term is the same input (X = a X + B X)
+  staged_epilogue<T, SYM, CIN, NW, EPI_PITCH, !SYM, TS, CV && CIN>(p, acc, reinterpret_cast<float *>(lds), g, tm,
+                                                                    tn, wm, wn, lane, tid);
   __syncthreads();  // the staging area is read before the next tile's loads overwrite it
   }
 }
@@ -1378,21 +1393,31 @@ static hipError_t launch_256(const GemmArgs &a, hipStream_t s) {
     if (a.a_trans != a.b_trans && (SYM || a.a_trans)) return hipErrorInvalidValue;
     const int mode = a.a_trans ? 2 : (a.b_trans ? 1 : 0);
 #define NSG_H(C, AT_, BT_) hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, C, AT_, BT_>), dim3(grid), dim3(256), 0, s, a)
-#define NSG_HS(AT_, BT_, S_) \
-  hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, false, AT_, BT_, S_>), dim3(grid), dim3(256), 0, s, a)
+#define NSG_HS(C, AT_, BT_, S_) \
+  hipLaunchKernelGGL((gemm256h_kernel<DT, SYM, C, AT_, BT_, S_>), dim3(grid), dim3(256), 0, s, a)
     if (a.src != kSrcPlain) {
       // an operand from the caller's bf16 input: converted (general fp16
-      // products, X0 as A of a row-major pair or as the K-major B) or raw
-      // (symmetric bf16 products)
-      if (a.Cin != nullptr || a.gscale == nullptr) return hipErrorInvalidValue;
+      // products, X0 as A of a row-major pair or as the K-major B, and as
+      // the Cin of X = a X + B X) or raw (symmetric bf16 products)
+      if (a.gscale == nullptr) return hipErrorInvalidValue;
       if constexpr (DT == NSG_F16 && !SYM) {
-        if (a.src == kSrcCvtA && mode == 0) NSG_HS(false, false, kSrcCvtA);
-        else if (a.src == kSrcCvtB && mode == 1) NSG_HS(false, true, kSrcCvtB);
-        else return hipErrorInvalidValue;
+        const void *x0 = a.src == kSrcCvtA ? a.A : a.B;
+        if (a.Cin != nullptr && a.Cin != x0) return hipErrorInvalidValue;
+        const bool c = a.Cin != nullptr;
+        if (a.src == kSrcCvtA && mode == 0) {
+          if (c) NSG_HS(true, false, false, kSrcCvtA);
+          else NSG_HS(false, false, false, kSrcCvtA);
+        } else if (a.src == kSrcCvtB && mode == 1) {
+          if (c) NSG_HS(true, false, true, kSrcCvtB);
+          else NSG_HS(false, false, true, kSrcCvtB);
+        } else {
+          return hipErrorInvalidValue;
+        }
       } else if constexpr (DT == NSG_BF16 && SYM) {
-        if (a.src != kSrcRaw || a.fb == nullptr || a.A != a.B || a.lda != a.ldb) return hipErrorInvalidValue;
-        if (mode == 0) NSG_HS(false, false, kSrcRaw);
-        else NSG_HS(true, true, kSrcRaw);
+        if (a.src != kSrcRaw || a.Cin != nullptr || a.fb == nullptr || a.A != a.B || a.lda != a.ldb)
+          return hipErrorInvalidValue;
+        if (mode == 0) NSG_HS(false, false, false, kSrcRaw);
+        else NSG_HS(false, true, true, kSrcRaw);
       } else {
         return hipErrorInvalidValue;
       }

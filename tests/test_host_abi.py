@@ -381,12 +381,12 @@ def test_in_place_plan():
 
 
 def test_bf16_input_plan():
-    """A bf16 input under fp16 compute in Gram mode, both sides multiples of
-    256, 512 <= n < 2048: the scale pass writes no copy, R0 = X0 X0^T
-    multiplies the raw bf16 input (source 3) and the general products that
-    read X0 convert it (source 1 for A, 2 for the K-major B); everything else
-    is the plan of an fp16 input.  Standard mode, square inputs and n >= 2048
-    keep the copy."""
+    """A bf16 input under fp16 compute, both sides multiples of 256,
+    512 <= n < 2048: the scale pass writes no copy, the first X X^T (R0, or
+    the standard step's A) multiplies the raw bf16 input (source 3) and the
+    general products that read X0 convert it (source 1 for A, 2 for the
+    K-major B); everything else is the plan of an fp16 input.  n >= 2048,
+    ragged sides, n < 512 and bf16 compute keep the copy."""
     def desc(P):
         return [(e["label"], e["kernel"], e["flops"], e["a_kmajor"], e["b_kmajor"], e["bytes"]) for e in P]
     for R, C, kw, x0_readers in (
@@ -395,14 +395,18 @@ def test_bf16_input_plan():
             (4096, 1536, {}, {"R0=XXt": 3, "Xt=XtQt": 1}),
             (2048, 512, dict(restart_after=0), {"R0=XXt": 3, "Yt=XtQt": 1}),
             (512, 2048, dict(steps=1), {"R0=XXt": 3, "Y=QX": 2}),
-            (512, 1024, dict(steps=8, restarts=[3, 5]), {"R0=XXt": 3, "X=QX": 2})):
+            (512, 1024, dict(steps=8, restarts=[3, 5]), {"R0=XXt": 3, "X=QX": 2}),
+            (768, 768, {}, {"A=XXt": 3, "X=aX+BX": 2}),
+            (2048, 512, dict(mode="standard"), {"A=XXt": 3, "Xt=aXt+XtB": 1}),
+            (512, 1536, dict(mode="standard"), {"A=XXt": 3, "X=aX+BX": 2}),
+            (1536, 1536, dict(steps=1), {"A=XXt": 3, "Y=aX+BX": 2})):
         P = nsg.plan(R, C, in_dtype="bf16", **kw)
         assert P[1]["label"] == "scales" and P[1]["bytes"] == 0
         sources = [(e["label"], e["source"]) for e in P if e["source"]]
         # exactly the first launch of each X0 reader (a later restart reads X1)
         assert dict(sources) == x0_readers and len(sources) == len(x0_readers), sources
         assert desc(P)[2:] == desc(nsg.plan(R, C, in_dtype="f16", **kw))[2:]
-    for R, C, kw in ((4096, 4096, {}), (2048, 512, dict(mode="standard")), (2048, 512, dict(compute_dtype="bf16")),
+    for R, C, kw in ((4096, 4096, {}), (2048, 2048, {}), (2048, 512, dict(compute_dtype="bf16")),
                      (2000, 512, {}), (256, 1024, {}), (11008, 4096, {}), (2048, 8192, {})):
         P = nsg.plan(R, C, in_dtype="bf16", **kw)
         assert all(e["source"] == 0 for e in P), (R, C, kw)
