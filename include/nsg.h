@@ -123,17 +123,16 @@ nsg_status_t ns_workspace_size(int64_t G, int64_t R, int64_t C,
  *           the products read X0 = G 2^e straight from `in` (the exact power
  *           of two rides in their fp32 epilogue scale) and no scaled copy is
  *           written; the results are the same either way.
- *           Under the same conditions a bf16 input with fp16 compute in Gram
- *           mode with 512 <= min(R, C) < 2048 is read in place too (larger
- *           buckets are bound by the MFMAs and keep the copy, which is then
- *           faster): the products that read X0
- *           convert the bf16 values to the fp16 X0 the copy would hold, and
- *           R0 = X0 X0^T multiplies the bf16 values themselves (their
- *           products are exact in fp32, so R0 is at least as accurate as from
- *           the fp16 copy; entries of X0 below fp16's normal range keep their
- *           bits).  A matrix with |G|_F outside about [2^-20, 2^45] (where
+ *           Under the same conditions a bf16 input with fp16 compute and
+ *           512 <= min(R, C) < 2048 is read in place too (larger buckets are
+ *           bound by the MFMAs and keep the copy, which is then faster): the
+ *           products that read X0 convert the bf16 values to the fp16 X0 the
+ *           copy would hold, and the first X0 X0^T (Gram R0, or the standard
+ *           step's A) multiplies the bf16 values themselves (their products
+ *           are exact in fp32, so it is at least as accurate as from the fp16
+ *           copy; entries of X0 below fp16's normal range keep their bits).  A matrix with |G|_F outside about [2^-20, 2^45] (where
  *           fp32 sums of raw products could overflow or small products
- *           flush) takes a scaled bf16 copy for R0 instead.
+ *           flush) takes a scaled bf16 copy for that product instead.
  *   out     device, [G, R, C] row-major contiguous, dtype out_dtype; may be
  *           the same memory as `in` (the input is then fully consumed into
  *           the workspace before the first output write); any other overlap

@@ -29,7 +29,8 @@ enum BufferKind : int { kInUser = -3, kOutUser = -2, kNone = -1 };
 //   kSrcCvtA / kSrcCvtB (fp16 kernel, general products): A (or B) is the
 //     caller's bf16 input; its K-slices are loaded raw into LDS and each wave
 //     converts the blocks it loaded to X_stored = RNE_fp16(x 2^e[b]), the
-//     value the scale pass would have stored, before the MFMAs read them.
+//     value the scale pass would have stored, before the MFMAs read them.  A
+//     Cin, if given, is that input too and is converted in the epilogue.
 //   kSrcRaw (bf16 kernel, symmetric products, fp16 outputs): A = B = the
 //     caller's bf16 input G, whose products are exact in fp32, with alpha'
 //     times 2^(gpow e[b]), for every matrix whose exponent passes
