@@ -124,7 +124,7 @@ nsg_status_t ns_workspace_size(int64_t G, int64_t R, int64_t C,
  *           of two rides in their fp32 epilogue scale) and no scaled copy is
  *           written; the results are the same either way.
  *           Under the same conditions a bf16 input with fp16 compute and
- *           512 <= min(R, C) < 2048 is read in place too (larger buckets are
+ *           256 <= min(R, C) < 2048 is read in place too (larger buckets are
  *           bound by the MFMAs and keep the copy, which is then faster): the
  *           products that read X0 convert the bf16 values to the fp16 X0 the
  *           copy would hold, and the first X0 X0^T (Gram R0, or the standard

@@ -328,8 +328,9 @@ def test_noalloc_rejects_before_any_gpu_call():
 def test_single_layout_plan():
     """The 16-bit 256 x 256 path keeps X in one layout only (the input's own):
     a tall input's Gram products read X^T K-major, a wide input's Q X reads X
-    K-major, and no transposed copy of X is stored; the fp32 path and small n
-    (128 x 128 kernel) keep both layouts and row-major operands only."""
+    K-major, and no transposed copy of X is stored; the fp32 path and n <= 128
+    (128 x 128 kernel) keep both layouts and row-major operands only; n = 200
+    takes the 256 x 256 path."""
     def km(P):
         return {e["label"]: (e["a_kmajor"], e["b_kmajor"]) for e in P if e["kernel"].startswith("gemm")}
     tall = km(nsg.plan(11008, 4096))
@@ -343,8 +344,9 @@ def test_single_layout_plan():
     assert all(e["b_kmajor"] and not e["a_kmajor"] for e in sq if e["label"] in ("X=aX+BX", "Y=aX+BX"))
     tall_std = km(nsg.plan(4096, 1024, mode="standard"))
     assert tall_std["A=XXt"] == (True, True) and tall_std["Xt=aXt+XtB"] == (False, False)
-    for P in (nsg.plan(11008, 4096, compute_dtype="f32"), nsg.plan(200, 1000)):
+    for P in (nsg.plan(11008, 4096, compute_dtype="f32"), nsg.plan(100, 1000), nsg.plan(1000, 128)):
         assert not any(e["a_kmajor"] or e["b_kmajor"] for e in P)
+    assert km(nsg.plan(200, 1000))["X=QX"] == (False, True)
     # one copy of X (and of X after the restart) instead of two
     n, m, es = 4096, 11008, 2
     x_bytes = m * (n + 64) * es
@@ -356,8 +358,8 @@ def test_in_place_plan():
     """A 16-bit input in the compute dtype with both sides multiples of 256 is
     read in place: the scale pass only finds the scales and writes no copy
     (no bytes), the launches and the other entries are unchanged, and so is
-    the workspace.  A bf16 input with fp16 compute, a ragged side, fp32
-    compute and the 128 x 128 path (n < 512) keep the copy."""
+    the workspace.  A ragged side, fp32 compute and the 128 x 128 path
+    (n <= 128) keep the copy."""
     def desc(P):
         return [(e["label"], e["kernel"], e["flops"], e["a_kmajor"], e["b_kmajor"]) for e in P]
     for R, C, kw in ((2048, 512, {}), (768, 3072, {}), (4096, 4096, {}), (2048, 512, dict(mode="standard")),
@@ -372,21 +374,24 @@ def test_in_place_plan():
         assert all(e["source"] == 0 for e in direct + copy)
     # the norm reads the input in its own dtype
     assert nsg.plan(2048, 512, in_dtype="f32")[0]["bytes"] == 2048 * 512 * 4
-    for R, C, kw in ((2000, 512, {}), (768, 3000, {}), (2048, 512, dict(compute_dtype="f32")), (2048, 256, {}),
-                     (256, 1024, {})):
+    for R, C, kw in ((2000, 512, {}), (768, 3000, {}), (2048, 512, dict(compute_dtype="f32")), (2048, 128, {}),
+                     (128, 1024, {})):
         assert nsg.plan(R, C, in_dtype=kw.get("compute_dtype", "f16"), **kw)[1]["label"] == "scale_cast_T"
         assert nsg.plan(R, C, in_dtype="bf16", **kw)[1]["label"] == "scale_cast_T"
+    # n = 256 runs on the 256 x 256 kernel and is read in place as well
+    for R, C in ((2048, 256), (256, 1024)):
+        assert nsg.plan(R, C, in_dtype="f16")[1]["label"] == "scales"
     with pytest.raises(nsg.NSGError):
         nsg.plan(2048, 512, in_dtype=7)
 
 
 def test_bf16_input_plan():
     """A bf16 input under fp16 compute, both sides multiples of 256,
-    512 <= n < 2048: the scale pass writes no copy, the first X X^T (R0, or
+    256 <= n < 2048: the scale pass writes no copy, the first X X^T (R0, or
     the standard step's A) multiplies the raw bf16 input (source 3) and the
     general products that read X0 convert it (source 1 for A, 2 for the
     K-major B); everything else is the plan of an fp16 input.  n >= 2048,
-    ragged sides, n < 512 and bf16 compute keep the copy."""
+    ragged sides, n <= 128 and bf16 compute keep the copy."""
     def desc(P):
         return [(e["label"], e["kernel"], e["flops"], e["a_kmajor"], e["b_kmajor"], e["bytes"]) for e in P]
     for R, C, kw, x0_readers in (
@@ -399,7 +404,8 @@ def test_bf16_input_plan():
             (768, 768, {}, {"A=XXt": 3, "X=aX+BX": 2}),
             (2048, 512, dict(mode="standard"), {"A=XXt": 3, "Xt=aXt+XtB": 1}),
             (512, 1536, dict(mode="standard"), {"A=XXt": 3, "X=aX+BX": 2}),
-            (1536, 1536, dict(steps=1), {"A=XXt": 3, "Y=aX+BX": 2})):
+            (1536, 1536, dict(steps=1), {"A=XXt": 3, "Y=aX+BX": 2}),
+            (256, 1024, {}, {"R0=XXt": 3, "X=QX": 2})):
         P = nsg.plan(R, C, in_dtype="bf16", **kw)
         assert P[1]["label"] == "scales" and P[1]["bytes"] == 0
         sources = [(e["label"], e["source"]) for e in P if e["source"]]
@@ -407,7 +413,7 @@ def test_bf16_input_plan():
         assert dict(sources) == x0_readers and len(sources) == len(x0_readers), sources
         assert desc(P)[2:] == desc(nsg.plan(R, C, in_dtype="f16", **kw))[2:]
     for R, C, kw in ((4096, 4096, {}), (2048, 2048, {}), (2048, 512, dict(compute_dtype="bf16")),
-                     (2000, 512, {}), (256, 1024, {}), (11008, 4096, {}), (2048, 8192, {})):
+                     (2000, 512, {}), (128, 1024, {}), (11008, 4096, {}), (2048, 8192, {})):
         P = nsg.plan(R, C, in_dtype="bf16", **kw)
         assert all(e["source"] == 0 for e in P), (R, C, kw)
         assert P[1]["label"] == ("scales" if kw.get("compute_dtype") == "bf16" else "scale_cast_T")
