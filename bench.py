@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -357,9 +358,12 @@ def bench_blas(args, w, dev):
     print(json.dumps({"vendor_blas_fp16": res, "workload": w.name, "G": G, "n": n, "m": m}), flush=True)
 
 
-def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False):
+def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False, min_seconds=0.0):
     """Warm up, then time `steps` whole calls with per-launch HIP events from the
-    library; returns (result dict, input on the host, GPU output)."""
+    library; returns (result dict, input on the host, GPU output).  With
+    min_seconds > 0, `steps` grows (up to 1000) until the timed calls take
+    about that long at the warm-up calls' pace, so that one slow call cannot
+    dominate a short bucket's rate."""
     import torch
 
     import newton_schulz_gram_amd as nsg
@@ -385,9 +389,13 @@ def time_workload(w, dev, steps, warmup, sym_updates=True, calibrate_copy=False)
         torch.cuda.synchronize()
         del src, dst
 
+    t_w = time.perf_counter()
     for _ in range(warmup):
         nsg.orthogonalize(x, out=out, workspace=ws, status=status, **kw)
     torch.cuda.synchronize()
+    if min_seconds > 0 and warmup > 0:
+        per_call = (time.perf_counter() - t_w) / warmup
+        steps = max(steps, min(1000, int(math.ceil(min_seconds / max(per_call, 1e-6)))))
 
     # timed region: `steps` whole calls, one event between calls and none
     # inside them (the library's per-launch events add a marker pair to every
@@ -585,8 +593,9 @@ def main():
         for name in OTHER_CONFIGS:
             wo = synth.WORKLOADS[name]
             steps = min(args.steps, 10)
-            log(f"timing {name}: {min(args.warmup, 3)} warm-up + {steps} timed calls")
-            r, xo, oo = time_workload(wo, dev, steps, min(args.warmup, 3), not args.general_updates)
+            log(f"timing {name}: {min(args.warmup, 3)} warm-up + at least {steps} timed calls (about 0.1 s)")
+            r, xo, oo = time_workload(wo, dev, steps, max(1, min(args.warmup, 3)), not args.general_updates,
+                                      min_seconds=0.1)
             if not args.no_cpu_baseline:
                 idx = PARITY_SAMPLE[name]
                 t0 = time.perf_counter()
